@@ -1,0 +1,444 @@
+"""Pins for the CPU oracle: each test ties the oracle to something other than
+itself -- a textbook identity, a library routine, a closed form, the numbers
+printed on the SignRot explainer page, or brute force on tiny inputs.
+
+Pages cited: the SignRot abstract (arXiv 2611.16502) and the explainer page
+"SignRot for 4-bit LLM quantization -- Sign-adjusted Hadamard rotation"
+(paragraphs on the quantizer, on rotation, on the failure mode, on the sign
+adjustment, on symmetric vs asymmetric quantizers, and the worked example).
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle as O
+import signrot_workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------
+# Hadamard construction
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("k", range(1, 10))
+def test_sylvester_is_scipy_hadamard(k):
+    assert np.array_equal(O.sylvester(k).astype(np.int64), scipy.linalg.hadamard(1 << k))
+
+
+def test_paley28_is_skew_hadamard():
+    h = O.paley28().astype(np.int64)
+    assert h.shape == (28, 28)
+    assert set(np.unique(h)) == {-1, 1}
+    assert np.array_equal(h @ h.T, 28 * np.eye(28, dtype=np.int64))
+    # skew type: H + H^T = 2I, so H is not symmetric
+    assert np.array_equal(h + h.T, 2 * np.eye(28, dtype=np.int64))
+    assert np.all(h[0] == 1)
+
+
+def test_gf27_field_axioms():
+    """The multiplication used for the quadratic character is a field: every
+    nonzero element has an inverse and exactly 13 nonzero squares exist."""
+    els = O.gf27_elements()
+    one = (1, 0, 0)
+    nz = [e for e in els if e != (0, 0, 0)]
+    for a in nz:
+        assert sum(O.signrot_oracle._gf27_mul(a, b) == one for b in nz) == 1
+    assert len({O.signrot_oracle._gf27_mul(a, a) for a in nz}) == 13
+    # associativity/commutativity on a sample
+    rng = np.random.default_rng(0)
+    mul = O.signrot_oracle._gf27_mul
+    for _ in range(200):
+        a, b, c = (els[i] for i in rng.integers(0, 27, 3))
+        assert mul(a, b) == mul(b, a)
+        assert mul(mul(a, b), c) == mul(a, mul(b, c))
+
+
+SMALL_N = [2, 4, 8, 16, 32, 64, 128, 28, 56, 112, 224, 448]
+
+
+@pytest.mark.parametrize("n", SMALL_N)
+def test_dense_hadamard_orthogonal(n):
+    h = O.hadamard(n).astype(np.int64)
+    assert np.array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 14336, 28672])
+def test_large_hadamard_sampled_rows_orthogonal(n):
+    rng = np.random.default_rng(n)
+    rows = rng.choice(n, size=12, replace=False)
+    r = np.stack([O.hadamard_row(n, int(c)).astype(np.int64) for c in rows])
+    assert np.array_equal(r @ r.T, n * np.eye(len(rows), dtype=np.int64))
+    # the column-block builder agrees with the row builder (H[i, j] both ways)
+    cols = O.hadamard_cols(n, 0, 256)
+    for i, c in enumerate(rows):
+        assert np.array_equal(cols[c], r[i, :256].astype(np.float64))
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16, 32, 64])
+def test_textbook_fwht_equals_dense_product(n):
+    x = np.random.default_rng(n).standard_normal((5, n))
+    y = O.rotate(x) * math.sqrt(n)
+    assert np.allclose(O.fwht_textbook(x), y, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [28, 56, 112])
+def test_kronecker_two_stage_equals_dense(n):
+    """x.H for H = H28 (x) H_{2^k} equals: mix the 28 blocks of 2^k by H28
+    (block a feeds block a' with weight H28[a, a']), then a textbook FWHT
+    inside every block."""
+    k = (n // 28).bit_length() - 1
+    x = np.random.default_rng(n).standard_normal((3, n))
+    h28 = O.paley28().astype(np.float64)
+    blocks = x.reshape(3, 28, 1 << k)
+    mixed = np.einsum("tab,ac->tcb", blocks, h28)
+    two_stage = O.fwht_textbook(mixed).reshape(3, n)
+    assert np.allclose(two_stage, O.rotate(x) * math.sqrt(n), rtol=0, atol=1e-12)
+
+
+def test_brute_force_n2_n4():
+    x = np.array([[3.0, 5.0, -2.0, 7.0]])
+    y4 = O.rotate(x) * 2.0
+    # by hand: rows of H4 in natural order are ++++, +-+-, ++--, +--+ (symmetric)
+    assert np.allclose(y4, [[13.0, -11.0, 3.0, 7.0]])
+    y2 = O.rotate(np.array([[1.0, 2.0]]))
+    assert np.allclose(y2, [[3 / math.sqrt(2), -1 / math.sqrt(2)]])
+
+
+def test_row_vector_orientation_is_observable_for_paley():
+    """y = x.H uses row c of H for a one-hot input at c; H.x would use column
+    c.  For the skew Paley factor these differ, so the convention is pinned."""
+    n = 28
+    x = np.zeros((1, n))
+    x[0, 5] = 1.0
+    y = O.rotate(x)[0] * math.sqrt(n)
+    h = O.hadamard(n).astype(np.float64)
+    assert np.array_equal(y, h[5])
+    assert not np.array_equal(y, h[:, 5])
+
+
+# --------------------------------------------------------------------------
+# The pages' closed form and worked example
+# --------------------------------------------------------------------------
+
+
+def test_closed_form_shift_printed_value():
+    """Failure-mode paragraph: a lone outlier M contributes +-M/sqrt(n) to every
+    output; the page prints 1510/sqrt(11008) as about 14.39."""
+    g = _golden("explainer_worked_token.json")
+    shift = g["outlier_M"] / math.sqrt(g["n"])
+    assert round(shift, 2) == g["shift_M_over_sqrt_n"]
+
+
+@pytest.mark.parametrize("n,c", [(4096, 1234), (14336, 2090), (28, 3), (8192, 0)])
+def test_closed_form_lone_outlier(n, c):
+    """x = M e_c -> |y_j| = M/sqrt(n) for every j, with signs = row c of H.
+    At n = 4096 and the page's M = 1510 this is exactly 1510/64 = 23.59375."""
+    x = np.zeros((1, n))
+    x[0, c] = 1510.0
+    y = O.rotate(x)[0]
+    assert np.allclose(np.abs(y), 1510.0 / math.sqrt(n), rtol=1e-15, atol=0)
+    assert np.array_equal(np.sign(y), O.hadamard_row(n, c).astype(np.float64))
+    if n == 4096:
+        assert np.all(np.abs(y) == 23.59375)
+    # the same through bf16: 1510 rounds to 1512 (bf16 spacing is 8 there)
+    M = 1512.0
+    bits = np.zeros((1, n), dtype=np.uint16)
+    bits[0, c] = W.f32_to_bf16_bits(np.array([1510.0], np.float32))[0]
+    assert O.bf16_bits_to_f64(bits)[0, c] == M
+    # after the SignRot flip the row is the constant sigma*M/sqrt(n) ...
+    cal = O.calibrate(bits)
+    assert cal["c"] == c and cal["sigma"] == 1
+    yd = O.rotate(O.bf16_bits_to_f64(bits), cal["d"])[0]
+    assert np.allclose(yd, M / math.sqrt(n), rtol=1e-15, atol=0)
+    # ... a degenerate range: s = 1, z = -min, every code 0, and the
+    # dequantized row is that constant.
+    q, s, z = O.quant_asym(yd[None, :])
+    assert s[0] == 1.0 and np.all(q == 0)
+    assert np.allclose(O.dequant(q, s, z)[0], yd)
+
+
+def _page_row(signs):
+    """A row whose magnitudes span exactly the page's [13.13, 15.63]."""
+    mags = np.array([13.13, 15.63, 13.13, 15.63, 14.0, 14.5, 13.5, 15.0])
+    return (mags * np.asarray(signs, np.float64))[None, :]
+
+
+def test_worked_example_printed_steps():
+    """'Worked example': symmetric step 15.63/7 ~ 2.23 (max error ~1.12, only the
+    levels at +-13.40 and +-15.63 used, 11 of 15 empty); asymmetric without the
+    flip 31.26/15 ~ 2.08; flip + asymmetric 2.50/15 ~ 0.167 (max error ~0.083);
+    roughly 13x finer."""
+    g = _golden("explainer_worked_token.json")
+    plain = _page_row([1, 1, -1, -1, -1, 1, -1, 1])  # both crowds present
+    flipped = np.abs(plain)  # the sign adjustment puts every value on one side
+
+    qs, ss = O.quant_sym(plain)
+    assert round(ss[0], 2) == g["sym_step"]
+    assert round(ss[0] / 2, 2) == g["sym_max_error"]
+    used = np.unique(np.abs(qs))
+    assert set(used.tolist()) == {6, 7}
+    assert sorted(np.round(used * ss[0], 2).tolist()) == g["sym_occupied_level_values"]
+    all_levels = set(range(-7, 8))
+    assert len(all_levels) == g["sym_levels_total"]
+    assert len(all_levels - set(np.unique(qs).tolist())) == g["sym_levels_empty"]
+    assert np.max(np.abs(plain - O.dequant_sym(qs, ss))) <= ss[0] / 2 + 1e-12
+
+    qa, sa, za = O.quant_asym(plain)
+    assert round(sa[0], 2) == g["asym_noflip_step"]
+
+    qf, sf, zf = O.quant_asym(flipped)
+    assert round(sf[0] * 15, 2) == g["signrot_asym_range_width"]
+    assert round(sf[0], 3) == g["signrot_asym_step"]
+    assert round(sf[0] / 2, 3) == g["signrot_asym_max_error"]
+    assert np.max(np.abs(flipped - O.dequant(qf, sf, zf))) <= sf[0] / 2 + 1e-12
+    assert round(ss[0] / sf[0]) == g["step_ratio_about"]
+    # the flip alone does nothing for the symmetric quantizer
+    qs2, ss2 = O.quant_sym(flipped)
+    assert ss2[0] == ss[0]
+
+
+def test_worked_example_replica_at_14336():
+    """A synthetic token shaped like the page's: one outlier whose share
+    M/sqrt(n) ~ 14.4 dominates Gaussian background; after plain rotation the
+    magnitudes form two crowds near +-14.4, after SignRot one crowd."""
+    n = 14336
+    rng = np.random.default_rng(47)
+    x = rng.standard_normal(n) * 0.32
+    c = 777
+    x[c] = 1720.0
+    bits = W.f32_to_bf16_bits(x.astype(np.float32))[None, :]
+    xb = O.bf16_bits_to_f64(bits)
+    cal = O.calibrate(bits)
+    assert cal["c"] == c
+    y_plain = O.rotate(xb)
+    y_sr = O.rotate(xb, cal["d"])
+    lo, hi = np.abs(y_plain).min(), np.abs(y_plain).max()
+    assert 12.5 < lo < 13.6 and 15.1 < hi < 16.2  # page: 13.13 .. 15.63
+    assert np.all(y_sr > 0)
+    _, ss = O.quant_sym(y_plain)
+    _, sa, _ = O.quant_asym(y_plain)
+    _, sf, _ = O.quant_asym(y_sr)
+    assert abs(ss[0] - 2.23) < 0.1
+    assert abs(sa[0] - 2.08) < 0.1
+    assert 0.12 < sf[0] < 0.22
+    assert 9 < ss[0] / sf[0] < 19
+
+
+# --------------------------------------------------------------------------
+# SignRot invariants
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,c,sigma", [(4096, 1234, 1), (14336, 9999, -1), (28672, 28671, 1), (56, 13, -1)])
+def test_flip_makes_outlier_row_constant(n, c, sigma):
+    """Sign-adjustment paragraph: after the flip the outlier row of H is all
+    one sign, so every output receives the outlier with one sign; D is its own
+    inverse."""
+    M = sigma * 1024.0
+    bits = np.zeros((1, n), dtype=np.uint16)
+    bits[0, c] = W.f32_to_bf16_bits(np.array([M], np.float32))[0]
+    cal = O.calibrate(bits)
+    assert (cal["c"], cal["sigma"]) == (c, sigma)
+    d = cal["d"].astype(np.int64)
+    row = O.hadamard_row(n, c).astype(np.int64)
+    assert np.all(row * d == sigma)  # x_c * H[c, j] * d_j = |x_c| for all j
+    assert np.all(d * d == 1)
+
+
+def test_symmetric_quantizer_ignores_the_flip():
+    """Symmetric-vs-asymmetric paragraph: flipping signs keeps every absolute
+    value, so the symmetric grid (sized by max |y|) is unchanged and the codes
+    flip with the values; the error is identical."""
+    bits, _ = W.batch("cfg1")
+    cal = O.calibrate(bits)
+    x = O.bf16_bits_to_f64(bits)
+    y = O.rotate(x)
+    yd = O.rotate(x, cal["d"])
+    assert np.allclose(yd, y * cal["d"][None, :], rtol=0, atol=0)
+    q, s = O.quant_sym(y)
+    qd, sd = O.quant_sym(yd)
+    assert np.array_equal(s, sd)
+    assert np.array_equal(qd, (q.astype(np.int64) * cal["d"][None, :]).astype(np.int8))
+    assert np.array_equal(O.mse(y, O.dequant_sym(q, s)), O.mse(yd, O.dequant_sym(qd, sd)))
+
+
+def test_rotation_is_orthogonal_mse_domain():
+    x = np.random.default_rng(5).standard_normal((4, 56))
+    y = O.rotate(x)
+    assert np.allclose((y * y).sum(1), (x * x).sum(1))
+
+
+# --------------------------------------------------------------------------
+# Quantizer, packing, dequantizer
+# --------------------------------------------------------------------------
+
+
+def test_quantizer_nearest_level_brute_force():
+    """Quantizer paragraph: 16 levels spread evenly from the token's smallest to
+    its largest value, each value snapped to the nearest level."""
+    rng = np.random.default_rng(11)
+    for trial in range(200):
+        n = int(rng.integers(2, 40))
+        y = rng.standard_normal((1, n)) * rng.uniform(0.01, 100) + rng.uniform(-50, 50)
+        q, s, z = O.quant_asym(y)
+        mn, mx = y.min(), y.max()
+        levels = mn + np.arange(16) * (mx - mn) / 15
+        d = np.abs(y[0][:, None] - levels[None, :])
+        best = d.min(axis=1)
+        chosen = d[np.arange(n), q[0]]
+        assert np.all(chosen <= best + 1e-12)
+        assert q[0][np.argmin(y[0])] == 0 and q[0][np.argmax(y[0])] == 15
+        assert np.all(q <= 15)
+        assert np.allclose(O.dequant(q, s, z)[0], levels[q[0]], rtol=1e-12, atol=1e-12)
+        assert np.max(np.abs(y - O.dequant(q, s, z))) <= s[0] / 2 * (1 + 1e-12)
+
+
+def test_zero_point_is_unrounded_and_may_leave_code_range():
+    y = np.array([[100.0, 101.0, 102.5]])
+    q, s, z = O.quant_asym(y)
+    assert s[0] == pytest.approx(2.5 / 15)
+    assert z[0] == pytest.approx(-100.0 / (2.5 / 15))
+    assert z[0] < -500  # far outside 0..15: the zero-point is a float
+
+
+def test_round_half_even_on_exact_ties():
+    # range 0..15 with s = 1: values 0.5, 1.5, 2.5 round to 0, 2, 2
+    y = np.array([[0.0, 0.5, 1.5, 2.5, 15.0]])
+    q, s, _ = O.quant_asym(y)
+    assert s[0] == 1.0
+    assert q[0].tolist() == [0, 0, 2, 2, 15]
+
+
+def test_pack_unpack_roundtrip_and_nibble_order():
+    q = np.array([[1, 2, 15, 0, 7, 8]], dtype=np.uint8)
+    p = O.pack_int4(q)
+    assert p.tolist() == [[0x21, 0x0F, 0x87]]
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 16, (5, 64)).astype(np.uint8)
+    assert np.array_equal(O.unpack_int4(O.pack_int4(q)), q)
+
+
+def test_f32_and_f64_quantizers_agree_away_from_boundaries():
+    bits, _ = W.batch("cfg1")
+    y = O.rotate(O.bf16_bits_to_f64(bits), O.calibrate(bits)["d"])
+    q64, s64, z64 = O.quant_asym(y, "f64")
+    q32, s32, z32 = O.quant_asym(y, "f32")
+    pos = O.code_position(y)
+    near = np.abs(pos - np.floor(pos) - 0.5) < 1e-4
+    assert np.array_equal(q64[~near], q32[~near])
+    assert np.allclose(s32, s64, rtol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Calibration
+# --------------------------------------------------------------------------
+
+
+def _bits(vals):
+    return W.f32_to_bf16_bits(np.asarray(vals, dtype=np.float32))
+
+
+def test_calibration_tie_breaks_and_sign():
+    # equal |x| in channels 3 and 1 -> channel 1; within channel 1, token 0
+    x = np.zeros((3, 8), np.float32)
+    x[2, 3] = -8.0
+    x[1, 1] = 8.0
+    x[2, 1] = -8.0
+    r = O.calibrate(_bits(x))
+    assert (r["c"], r["t"], r["m_c"], r["sigma"]) == (1, 1, 8.0, 1)
+    x[1, 1] = 0.5
+    r = O.calibrate(_bits(x))
+    assert (r["c"], r["t"], r["m_c"], r["sigma"]) == (1, 2, -8.0, -1)
+    # brute force over all (t, j) on random small batches with repeated values
+    rng = np.random.default_rng(9)
+    for _ in range(100):
+        xx = rng.integers(-4, 5, size=(4, 8)).astype(np.float32)
+        r = O.calibrate(_bits(xx))
+        best = max(itertools.product(range(4), range(8)),
+                   key=lambda tj: (abs(xx[tj]), -tj[1], -tj[0]))
+        assert (r["t"], r["c"]) == best
+
+
+def test_calibration_zero_batch_and_negative_zero():
+    z = np.zeros((2, 8), np.uint16)
+    r = O.calibrate(z)
+    assert (r["c"], r["t"], r["sigma"]) == (0, 0, 1)
+    z[0, 0] = 0x8000  # -0.0
+    assert O.calibrate(z)["sigma"] == 1
+    assert np.array_equal(r["d"], O.hadamard_row(8, 0))
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3"])
+def test_calibration_recovers_planted_channel(name):
+    cal_bits, meta = W.calibration_batch(name)
+    r = O.calibrate(cal_bits)
+    assert r["c"] == meta["channel"]
+    x = O.bf16_bits_to_f64(cal_bits)
+    assert r["m_c"] == x[r["t"], r["c"]]
+    assert r["sigma"] == (1 if r["m_c"] >= 0 else -1)
+
+
+# --------------------------------------------------------------------------
+# Statistical consequences the pages state
+# --------------------------------------------------------------------------
+
+
+def _codes_used_interval(q_row):
+    u = np.unique(q_row)
+    return u.max() - u.min() + 1 == len(u)
+
+
+def test_signrot_collapses_bimodal_tokens():
+    """Failure-mode and sign-adjustment paragraphs: a dominating outlier splits a
+    plainly rotated token into two crowds with an empty middle; after the flip
+    the token is one crowd (one sign, contiguous codes)."""
+    bits, meta = W.batch("cfg3", tokens=64)
+    cal = O.calibrate(W.calibration_batch("cfg3")[0])
+    rows = meta["outlier_tokens"][meta["outlier_tokens"] < 64]
+    assert len(rows) >= 5
+    x = O.bf16_bits_to_f64(bits[rows])
+    y_plain = O.rotate(x)
+    y_sr = O.rotate(x, cal["d"])
+    q_plain, _, _ = O.quant_asym(y_plain)
+    q_sr, _, _ = O.quant_asym(y_sr)
+    for i in range(len(rows)):
+        assert np.all(np.sign(y_sr[i]) == np.sign(y_sr[i][0]))
+        assert _codes_used_interval(q_sr[i])
+        assert not _codes_used_interval(q_plain[i])
+
+
+def test_mse_ordering_on_outlier_and_control_tokens():
+    """SignRot+asym beats plain+asym and plain+sym on outlier tokens; on tokens
+    without an outlier it is no worse in a statistically meaningful way."""
+    bits, meta = W.batch("cfg3", tokens=128)
+    cal = O.calibrate(W.calibration_batch("cfg3")[0])
+    x = O.bf16_bits_to_f64(bits)
+    y_plain = O.rotate(x)
+    y_sr = O.rotate(x, cal["d"])
+
+    def asym(y):
+        q, s, z = O.quant_asym(y)
+        return O.mse(y, O.dequant(q, s, z))
+
+    def sym(y):
+        q, s = O.quant_sym(y)
+        return O.mse(y, O.dequant_sym(q, s))
+
+    out = np.zeros(len(x), bool)
+    out[meta["outlier_tokens"][meta["outlier_tokens"] < len(x)]] = True
+    m_sr, m_pa, m_ps = asym(y_sr), asym(y_plain), sym(y_plain)
+    assert np.all(m_sr[out] < m_pa[out]) and np.all(m_sr[out] < m_ps[out])
+    assert m_sr[~out].mean() < 1.1 * m_pa[~out].mean()
