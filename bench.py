@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of SignRot's fused online path on one MI355X.
+
+One step = one call of signrot_rotate_quant_int4 over a whole batch: bf16
+activations in HBM -> Hadamard rotation -> sign flip -> per-token min/max ->
+scale, zero-point -> rounding -> packed int4 codes in HBM.  Calibration is an
+offline step and is not timed.
+
+Workload: n = 14336 (= 28 * 2^9, the LLaMA3-8B down-projection input width),
+8192 tokens per batch, background N(0, 0.7) with a massive outlier channel
+(M ~ U[800, 2500]) in 20% of tokens, seeded and synthetic.
+
+The inputs are copied to several device buffers whose total exceeds the
+256 MiB last-level (MALL) cache, and the steps cycle through them, so every
+step reads its input from HBM.
+
+Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
+--warmup W, --no-cpu-baseline, --pmc-copy (also run plain copies of known size
+for the counter calibration of a rocprofv3 --pmc run).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
+WORKLOAD = "target"
+BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
+
+
+def algorithmic_bytes_per_token(n: int) -> int:
+    # bf16 input + packed int4 codes + fp32 scale + fp32 zero-point
+    return 2 * n + n // 2 + 8
+
+
+def cpu_baseline(bits: np.ndarray, d: np.ndarray, budget_s: float = 12.0) -> dict:
+    """Time the oracle (numpy float64, as it stands) on a bounded sample of the
+    same workload: as many 64-token chunks as fit in ~budget_s seconds."""
+    import oracle as O
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=cores)
+    except Exception:  # pragma: no cover
+        threads = cores
+    chunk = 64
+    done = 0
+    t0 = time.perf_counter()
+    while done + chunk <= bits.shape[0]:
+        O.rotate_quant_int4(bits[done:done + chunk], d)
+        done += chunk
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} tokens of the same workload (n={bits.shape[1]}), "
+                      f"oracle rotate (float64 blocked dense product) + asymmetric INT4, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              "the path shards tokens across GPUs with no exchange, see the design notes.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import rotation_activation_quantization_amd as R
+    import signrot_workloads as W
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    L = R.lib()
+
+    w = W.WORKLOADS[WORKLOAD]
+    bits, meta = W.batch(WORKLOAD, tokens=args.tokens)
+    t, n = bits.shape
+    x0 = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    d, c, _, _ = R.calibrate(to_dev_bits(W.calibration_batch(WORKLOAD)[0], torch))
+
+    in_bytes = x0.numel() * 2
+    nsets = max(2, int(np.ceil(BUFFER_SETS_MIN_BYTES / in_bytes)))
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    outs = [(torch.empty((t, n // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty(t, dtype=torch.float32, device="cuda"),
+             torch.empty(t, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    calls = []
+    for i in range(nsets):
+        co, sc, ze = outs[i]
+        calls.append((xs[i].data_ptr(), t, n, n, d.data_ptr(), co.data_ptr(), sc.data_ptr(), ze.data_ptr(),
+                      None, sptr))
+    fn = L.signrot_rotate_quant_int4
+
+    def step(i):
+        st = fn(*calls[i % nsets])
+        if st != 0:
+            R.check(st, "signrot_rotate_quant_int4")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # per-launch HIP events on the stream the kernel runs on
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    if args.pmc_copy:
+        # plain copies of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = t * args.steps / wall
+    bpt = algorithmic_bytes_per_token(n)
+    avg_kernel_ms = float(kern_ms.mean())
+    achieved = bpt * t / (avg_kernel_ms * 1e-3) / 1e9
+    line = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak), fused SignRot rotate+INT4 quant",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"n={n} (28*2^9, LLaMA3-8B down_proj input) x {t} tokens bf16, N(0,0.7) background, "
+                        f"outlier channel {c} with M~U[{w.m_lo:g},{w.m_hi:g}] in {w.p_outlier:.0%} of tokens; "
+                        f"SignRot sign vector from calibration on {w.calib_tokens} tokens",
+            "n": n,
+            "tokens": t,
+            "parallelism": "single GPU",
+            "kernel": R.kernel_name(n),
+            "input_buffer_sets": nsets,
+            "hbm_gbs_wall": bpt * tokens_per_s / 1e9,
+            "pct_of_peak_hbm_wall": 100.0 * bpt * tokens_per_s / 1e9 / PEAK_HBM_GBS,
+            "kernel_ms_p10_p50_p90": [float(np.percentile(kern_ms, q)) for q in (10, 50, 90)],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": None,
+            "bytes_per_token": bpt,
+            "kernel_avg_ms": avg_kernel_ms,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy())
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def to_dev_bits(bits, torch):
+    t, n = bits.shape
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,143 @@
+/*
+ * signrot.h -- C ABI of libsignrot, SignRot's online activation path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: the SignRot abstract, arXiv 2611.16502, and the explainer
+ * "SignRot for 4-bit LLM quantization -- Sign-adjusted Hadamard rotation"):
+ * at the input of an LLM down-projection every token x (a row of n bf16
+ * values) is rotated by an orthonormal Hadamard matrix, y = x.H / sqrt(n)
+ * (explainer, paragraph on rotation: every entry of H is +-1/sqrt(n), applied
+ * with a fast Walsh-Hadamard transform, paragraph on the down-projection); the
+ * columns of H are sign-flipped by a calibrated vector d so that the one
+ * massive-outlier channel reaches every output with the same sign
+ * (explainer, paragraph on the sign adjustment; abstract); and the result is
+ * quantized per token to 16 evenly spaced levels between the token's minimum
+ * and maximum, an asymmetric INT4 code with a zero-point (explainer,
+ * paragraphs on the quantizer and on symmetric versus asymmetric quantizers).
+ *
+ * Hadamard order.  n = 2^k (1 <= k <= 15) uses the Sylvester matrix in natural
+ * order, H[i][j] = (-1)^popcount(i & j).  n = 28 * 2^k (0 <= k <= 10) uses
+ * H = H28 (x) H_{2^k} with index i = a * 2^k + b (a < 28, b < 2^k), where H28
+ * is Paley's construction I over GF(27) = GF(3)[t]/(t^3 + 2t + 1): H28 = I + S,
+ * S the Jacobsthal matrix of the quadratic character bordered by a row of +1
+ * and a column of -1.  The pages only fix "a Hadamard matrix"; these are the
+ * library's choices.  Orientation: y_j = sum_i x_i H[i][j] (x is a row
+ * vector; the outlier at channel c reaches the outputs through row c of H).
+ *
+ * Conventions shared by every call:
+ *   - All sizes are element counts.  Device pointers are plain HIP device
+ *     addresses (e.g. from torch).  `stream` is a hipStream_t passed as
+ *     void*; NULL means the default stream.  Every tensor is owned by the
+ *     caller; the library keeps no pointer after a call returns.
+ *   - Activations are bf16 bit patterns, row-major [tokens][ld], ld >= n,
+ *     with the base pointer 16-byte aligned and ld a multiple of 8 (so each
+ *     row starts 16-byte aligned).
+ *   - Calls return a signrot_status.  Argument errors are detected on the
+ *     host before any HIP call and leave every output untouched.  A HIP
+ *     error returns SIGNROT_EHIP; outputs are then unspecified and
+ *     signrot_last_error() holds the HIP message.  Nothing throws.
+ *   - tokens == 0 is a successful no-op (null pointers are then allowed).
+ *   - Non-finite inputs, or inputs so large that the rotated values overflow
+ *     binary32, give unspecified outputs (no checks on the hot path).
+ *   - Calls are reentrant; concurrent calls on different streams are allowed.
+ */
+#ifndef SIGNROT_H
+#define SIGNROT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SIGNROT_OK = 0,
+  SIGNROT_EINVAL = -1,          /* bad pointer, size, stride or alignment   */
+  SIGNROT_EUNSUPPORTED_N = -2,  /* n is neither 2^k nor 28 * 2^k in range    */
+  SIGNROT_EHIP = -3             /* a HIP runtime call or launch failed       */
+} signrot_status;
+
+/* 1 if n = 2^k (1 <= k <= 15) or n = 28 * 2^k (0 <= k <= 10), else 0. */
+int signrot_supported_n(int64_t n);
+
+/*
+ * Calibration (abstract: one calibration forward pass; explainer, paragraph
+ * on the sign adjustment: the channel with the largest absolute activation,
+ * and a flip of each column j of H by the sign of that row's entry).
+ *
+ *   x_bf16  device, [tokens][ld] bf16 calibration batch (tokens < 2^28).
+ *   d_out   device, [n] int8: d_j = sign(M_c) * H[c][j], values +1/-1, where
+ *           c is the channel of the largest |x| over the batch and M_c the
+ *           signed value there.  Ties: smallest channel, then smallest token.
+ *           sign(+0) = sign(-0) = +1.
+ *   c_out   host, may be NULL: the channel c.
+ *   t_out   host, may be NULL: the token t holding M_c.
+ *   mc_out  host, may be NULL: M_c widened to float.
+ *
+ * Enqueues its kernels on `stream`, then synchronizes that stream (the host
+ * outputs need the result).  Uses a 16-byte stream-ordered scratch buffer
+ * (hipMallocAsync / hipFreeAsync).  tokens == 0 -> SIGNROT_EINVAL (there is no
+ * channel to find).
+ */
+int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
+                      int8_t* d_out, int32_t* c_out, int64_t* t_out, float* mc_out,
+                      void* stream);
+
+/*
+ * The online path: y = (x . H / sqrt(n)) (.) d, then per-token asymmetric
+ * INT4 (explainer, paragraphs on rotation, on the sign adjustment and on the
+ * quantizer).  Per token, with mn = min_j y_j and mx = max_j y_j:
+ *   scale = (mx - mn) / 15, or 1 when mx == mn;
+ *   zero  = -mn / scale, in code units, neither rounded nor clamped;
+ *   q_j   = clamp(round((y_j - mn) / scale), 0, 15), round to nearest.
+ *
+ *   x_bf16  device, [tokens][ld] bf16.
+ *   d       device, [n] int8, every entry +1 or -1 (any other value gives
+ *           unspecified output).  When d = sigma * (row c of H) -- the form
+ *           signrot_calibrate produces -- the library recognises it and
+ *           evaluates the identical quantity as ((x - x_c e_c) . H) (.) d plus
+ *           the constant sigma * x_c / sqrt(n), so the outlier is added once
+ *           instead of being rounded through every butterfly stage.
+ *   codes   device, [tokens][n/2] uint8: code of channel 2m in the low nibble
+ *           of byte m, channel 2m+1 in the high nibble.
+ *   scale   device, [tokens] float.
+ *   zero    device, [tokens] float.
+ *   y_out   device, [tokens][n] float, or NULL: the rotated, flipped values
+ *           in binary32 (a debugging output; the codes do not depend on it).
+ *
+ * Asynchronous: returns once the kernel is enqueued on `stream`.  Arithmetic
+ * is binary32 throughout.
+ */
+int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
+                              const int8_t* d, uint8_t* codes, float* scale, float* zero,
+                              float* y_out, void* stream);
+
+/*
+ * Dequantization: y_hat[t][j] = scale[t] * (q_j - zero[t]), the level value
+ * of each code (mn + q * scale).  codes/scale/zero as produced above; y_hat
+ * device [tokens][n] float.  n must be supported.  Asynchronous.
+ */
+int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero,
+                    int64_t tokens, int64_t n, float* y_hat, void* stream);
+
+/* Static text for a status code. */
+const char* signrot_strerror(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* signrot_last_error(void);
+
+/*
+ * The library's own H28, row-major, entries +1/-1, written to host memory
+ * out[784].  Lets a test compare it with an independently built table.
+ */
+int signrot_debug_h28(int8_t* out);
+
+/* Which kernel variant signrot_rotate_quant_int4 would launch for n (a
+ * static string naming it), or NULL when n is unsupported. */
+const char* signrot_kernel_name(int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SIGNROT_H */

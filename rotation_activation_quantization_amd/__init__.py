@@ -1,0 +1,168 @@
+"""SignRot's online activation path on MI355X: Python binding of libsignrot.
+
+Argument marshalling only: every step of the path runs in the HIP library
+(`libsignrot.so`, built in-tree by `build.py`).  Torch supplies device memory
+and the current stream; nothing here computes on the CPU, and every call fails
+loudly when the library is missing.
+
+The C ABI is declared in include/signrot.h; the functions here keep its names.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsignrot.so")
+
+SIGNROT_OK = 0
+SIGNROT_EINVAL = -1
+SIGNROT_EUNSUPPORTED_N = -2
+SIGNROT_EHIP = -3
+
+_lib = None
+
+
+class SignRotError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status}: {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsignrot.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m rotation_activation_quantization_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    L.signrot_supported_n.argtypes = [i64]
+    L.signrot_supported_n.restype = ctypes.c_int
+    L.signrot_calibrate.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.signrot_calibrate.restype = ctypes.c_int
+    L.signrot_rotate_quant_int4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+    L.signrot_rotate_quant_int4.restype = ctypes.c_int
+    L.signrot_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+    L.signrot_dequant.restype = ctypes.c_int
+    L.signrot_strerror.argtypes = [ctypes.c_int]
+    L.signrot_strerror.restype = ctypes.c_char_p
+    L.signrot_last_error.argtypes = []
+    L.signrot_last_error.restype = ctypes.c_char_p
+    L.signrot_debug_h28.argtypes = [vp]
+    L.signrot_debug_h28.restype = ctypes.c_int
+    L.signrot_kernel_name.argtypes = [i64]
+    L.signrot_kernel_name.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+EXPORTED = (
+    "signrot_supported_n",
+    "signrot_calibrate",
+    "signrot_rotate_quant_int4",
+    "signrot_dequant",
+    "signrot_strerror",
+    "signrot_last_error",
+    "signrot_debug_h28",
+    "signrot_kernel_name",
+)
+
+
+def check(status: int, where: str) -> None:
+    if status != SIGNROT_OK:
+        L = lib()
+        detail = (L.signrot_last_error() or b"").decode() or L.signrot_strerror(status).decode()
+        raise SignRotError(status, where, detail)
+
+
+def supported_n(n: int) -> bool:
+    return bool(lib().signrot_supported_n(int(n)))
+
+
+def kernel_name(n: int) -> str | None:
+    r = lib().signrot_kernel_name(int(n))
+    return r.decode() if r else None
+
+
+def debug_h28():
+    """The library's own H28 as a 28x28 list of +-1 rows."""
+    buf = (ctypes.c_int8 * 784)()
+    check(lib().signrot_debug_h28(ctypes.addressof(buf)), "signrot_debug_h28")
+    return [list(buf[r * 28:(r + 1) * 28]) for r in range(28)]
+
+
+def _stream_of(t):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows(x):
+    """(pointer, tokens, n, ld) of a [T, n] bf16 tensor whose rows are contiguous."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda:
+        raise ValueError("x must be a 2-D bfloat16 CUDA tensor")
+    if x.shape[1] > 0 and x.stride(1) != 1:
+        raise ValueError("x rows must be contiguous")
+    ld = x.stride(0) if x.shape[0] > 1 else max(x.shape[1], (x.shape[1] + 7) // 8 * 8)
+    return x.data_ptr(), x.shape[0], x.shape[1], ld
+
+
+def signrot_calibrate(x):
+    """Calibrate on a bf16 batch [T, n] -> (d int8 [n] on the device, c, t, M_c)."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    d = torch.empty(n, dtype=torch.int8, device=x.device)
+    c = ctypes.c_int32()
+    tt = ctypes.c_int64()
+    m = ctypes.c_float()
+    check(lib().signrot_calibrate(ptr, t, n, ld, d.data_ptr(), ctypes.addressof(c), ctypes.addressof(tt),
+                                  ctypes.addressof(m), _stream_of(x)), "signrot_calibrate")
+    return d, c.value, tt.value, m.value
+
+
+def signrot_rotate_quant_int4(x, d, y_out: bool = False, out=None):
+    """bf16 [T, n] and d int8 [n] -> (codes u8 [T, n/2], scale f32 [T], zero f32 [T]
+    [, y f32 [T, n]]).  `out` may pass preallocated (codes, scale, zero[, y])."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    if d.dtype != torch.int8 or d.numel() != n or not d.is_contiguous():
+        raise ValueError("d must be a contiguous int8 tensor of n entries")
+    if out is None:
+        codes = torch.empty((t, n // 2), dtype=torch.uint8, device=x.device)
+        scale = torch.empty(t, dtype=torch.float32, device=x.device)
+        zero = torch.empty(t, dtype=torch.float32, device=x.device)
+        y = torch.empty((t, n), dtype=torch.float32, device=x.device) if y_out else None
+    else:
+        codes, scale, zero = out[:3]
+        y = out[3] if len(out) > 3 else None
+    check(lib().signrot_rotate_quant_int4(ptr, t, n, ld, d.data_ptr(), codes.data_ptr(), scale.data_ptr(),
+                                          zero.data_ptr(), y.data_ptr() if y is not None else None,
+                                          _stream_of(x)), "signrot_rotate_quant_int4")
+    return (codes, scale, zero, y) if y is not None else (codes, scale, zero)
+
+
+def signrot_dequant(codes, scale, zero, n: int | None = None):
+    """codes u8 [T, n/2], scale/zero f32 [T] -> y_hat f32 [T, n]."""
+    import torch
+
+    t = codes.shape[0]
+    n = codes.shape[1] * 2 if n is None else int(n)
+    y = torch.empty((t, n), dtype=torch.float32, device=codes.device)
+    check(lib().signrot_dequant(codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), t, n, y.data_ptr(),
+                                _stream_of(codes)), "signrot_dequant")
+    return y
+
+
+# short aliases
+calibrate = signrot_calibrate
+rotate_quant_int4 = signrot_rotate_quant_int4
+dequant = signrot_dequant

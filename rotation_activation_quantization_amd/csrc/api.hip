@@ -1,0 +1,199 @@
+// C ABI of libsignrot: argument validation, dispatch and error reporting.
+// Every check happens on the host before any HIP call; a failing HIP call is
+// reported as SIGNROT_EHIP with its message kept per thread.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/signrot.h"
+#include "internal.h"
+
+namespace signrot {
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, const char* detail) {
+  snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+}
+
+int fail_einval(const char* what) {
+  set_error("invalid argument: %s", what);
+  return SIGNROT_EINVAL;
+}
+
+int fail_hip(hipError_t e, const char* where) {
+  char buf[400];
+  snprintf(buf, sizeof(buf), "%s: %s (%d)", where, hipGetErrorString(e), static_cast<int>(e));
+  set_error("%s", buf);
+  return SIGNROT_EHIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+Shape factor_n(int64_t n) {
+  Shape s;
+  if (n < 2 || n > 32768) return s;
+  int64_t p = n;
+  bool m28 = false;
+  if (n % 28 == 0) {
+    m28 = true;
+    p = n / 28;
+  }
+  if (p & (p - 1)) return s;
+  int k = 0;
+  while ((int64_t{1} << k) < p) ++k;
+  if (m28 && k > 10) return s;
+  if (!m28 && (k < 1 || k > 15)) return s;
+  s.n = static_cast<int>(n);
+  s.k = k;
+  s.m28 = m28;
+  s.ok = true;
+  return s;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(cache.size())) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+}  // namespace signrot
+
+using namespace signrot;
+
+extern "C" {
+
+int signrot_supported_n(int64_t n) { return factor_n(n).ok ? 1 : 0; }
+
+const char* signrot_strerror(int status) {
+  switch (status) {
+    case SIGNROT_OK: return "ok";
+    case SIGNROT_EINVAL: return "invalid argument";
+    case SIGNROT_EUNSUPPORTED_N: return "unsupported n (need 2^k, 1<=k<=15, or 28*2^k, 0<=k<=10)";
+    case SIGNROT_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* signrot_last_error(void) { return g_last_error; }
+
+int signrot_debug_h28(int8_t* out) {
+  if (!out) return fail_einval("out is NULL");
+  memcpy(out, h28().h, 28 * 28);
+  return SIGNROT_OK;
+}
+
+const char* signrot_kernel_name(int64_t n) {
+  const Shape sh = factor_n(n);
+  if (!sh.ok) return nullptr;
+  return rq_generic_name();
+}
+
+int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
+                      int32_t* c_out, int64_t* t_out, float* mc_out, void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  if (!sh.ok) {
+    set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (tokens <= 0) return fail_einval("calibration needs tokens >= 1");
+  if (tokens >= (int64_t{1} << 28)) return fail_einval("tokens must be < 2^28");
+  if (!x_bf16 || !d_out) return fail_einval("null device pointer");
+  if (ld < n) return fail_einval("ld < n");
+  if (!aligned16(x_bf16) || (ld & 7)) return fail_einval("x must be 16-byte aligned and ld a multiple of 8");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long* scratch = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), 16, s);
+  if (e != hipSuccess) return fail_hip(e, "hipMallocAsync");
+  e = launch_calibrate(static_cast<const uint16_t*>(x_bf16), tokens, ld, sh, d_out, scratch, s);
+  unsigned long long host[2] = {0ull, 0ull};
+  if (e == hipSuccess) e = hipMemcpyAsync(host, scratch, sizeof(host), hipMemcpyDeviceToHost, s);
+  hipError_t ef = hipFreeAsync(scratch, s);
+  if (e == hipSuccess) e = ef;
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "calibrate");
+  const unsigned long long key = host[0];
+  const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
+  const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
+  const uint32_t mbits = static_cast<uint32_t>(host[1]) << 16;
+  float m;
+  memcpy(&m, &mbits, sizeof(m));
+  if (c_out) *c_out = c;
+  if (t_out) *t_out = t;
+  if (mc_out) *mc_out = m;
+  return SIGNROT_OK;
+}
+
+int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, const int8_t* d,
+                              uint8_t* codes, float* scale, float* zero, float* y_out, void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  if (!sh.ok) {
+    set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (tokens < 0) return fail_einval("tokens < 0");
+  if (ld < n) return fail_einval("ld < n");
+  if (ld & 7) return fail_einval("ld must be a multiple of 8");
+  if (tokens == 0) return SIGNROT_OK;
+  if (tokens > (int64_t{1} << 40)) return fail_einval("tokens too large");
+  if (!x_bf16 || !d || !codes || !scale || !zero) return fail_einval("null device pointer");
+  if (!aligned16(x_bf16)) return fail_einval("x must be 16-byte aligned");
+  RqArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.d = d;
+  a.codes = codes;
+  a.scale = scale;
+  a.zero = zero;
+  a.yout = y_out;
+  a.tokens = tokens;
+  a.ld = ld;
+  a.n = sh.n;
+  a.k = sh.k;
+  a.m28 = sh.m28 ? 1 : 0;
+  a.inv_sqrt_n = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
+  a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
+  for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  hipError_t e = launch_rq_generic(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4 launch");
+  return SIGNROT_OK;
+}
+
+int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens, int64_t n,
+                    float* y_hat, void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  if (!sh.ok) {
+    set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (tokens < 0) return fail_einval("tokens < 0");
+  if (tokens == 0) return SIGNROT_OK;
+  if (!codes || !scale || !zero || !y_hat) return fail_einval("null device pointer");
+  if (reinterpret_cast<uintptr_t>(y_hat) & 7u) return fail_einval("y_hat must be 8-byte aligned");
+  hipError_t e = launch_dequant(codes, scale, zero, tokens, sh.n, y_hat, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "dequant launch");
+  return SIGNROT_OK;
+}
+
+}  // extern "C"

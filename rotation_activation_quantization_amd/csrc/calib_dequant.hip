@@ -1,0 +1,125 @@
+// Calibration (outlier channel and sign vector) and dequantization kernels.
+//
+// Calibration follows the SignRot abstract (one calibration pass that finds
+// the massive-outlier channel and builds a sign vector) and the explainer's
+// paragraph on the sign adjustment (the channel with the largest absolute
+// activation; each column j of H is multiplied by the sign of that row's
+// entry).  The global argmax is one 64-bit key per element,
+//   key = |x| bits (15) << 48 | (2^20 - 1 - j) << 28 | (2^28 - 1 - t),
+// so the unsigned maximum is the largest |x|, then the smallest channel j,
+// then the smallest token t.  bf16 magnitudes order like their bit patterns.
+#include "device_common.h"
+
+namespace signrot {
+namespace {
+
+constexpr int kCalThreads = 256;
+
+__device__ __forceinline__ unsigned long long cal_key(uint32_t bits, int64_t t, int64_t j) {
+  return (static_cast<unsigned long long>(bits & 0x7fffu) << 48) |
+         (static_cast<unsigned long long>(0xfffffu - static_cast<uint32_t>(j)) << 28) |
+         static_cast<unsigned long long>(0x0fffffffu - static_cast<uint32_t>(t));
+}
+
+__global__ void cal_init_kernel(unsigned long long* scratch) {
+  if (threadIdx.x == 0) {
+    scratch[0] = 0ull;
+    scratch[1] = 0ull;
+  }
+}
+
+__global__ __launch_bounds__(kCalThreads) void cal_argmax_kernel(const uint16_t* x, int64_t tokens,
+                                                                 int64_t n, int64_t ld,
+                                                                 unsigned long long* scratch) {
+  __shared__ unsigned long long red[kCalThreads / 64];
+  unsigned long long best = 0ull;
+  const int64_t total = tokens * n;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = e / n, j = e - t * n;
+    const unsigned long long key = cal_key(x[t * ld + j], t, j);
+    best = key > best ? key : best;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long other = __shfl_xor(best, o);
+    best = other > best ? other : best;
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < kCalThreads / 64; ++i) best = red[i] > best ? red[i] : best;
+    atomicMax(&scratch[0], best);
+  }
+}
+
+// Fills d[j] = sigma * H[c][j]; also records the bf16 bits of M_c in scratch[1].
+__global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int m28,
+                                H28Masks masks, unsigned long long* scratch, int8_t* d) {
+  const unsigned long long key = scratch[0];
+  const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
+  const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
+  const uint32_t mbits = x[t * ld + c];
+  // sigma = sign(M_c), with sign(+-0) = +1
+  const uint32_t neg = ((mbits & 0x7fffu) != 0u) && ((mbits & 0x8000u) != 0u);
+  const int bmask = (1 << k) - 1;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
+    if (m28) bit ^= (masks.m[c >> k] >> (j >> k)) & 1u;
+    d[j] = (bit ^ neg) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) scratch[1] = mbits;
+}
+
+// y[t][j] = scale[t] * (q - zero[t]); one thread per code byte.
+__global__ void dequant_kernel(const uint8_t* codes, const float* scale, const float* zero,
+                               int64_t tokens, int n, float* y) {
+  const int64_t half = n / 2;
+  const int64_t total = tokens * half;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t t = e / half;
+    const uint32_t b = codes[e];
+    const float s = scale[t], z = zero[t];
+    float2 v;
+    v.x = s * (static_cast<float>(b & 15u) - z);
+    v.y = s * (static_cast<float>(b >> 4) - z);
+    *reinterpret_cast<float2*>(y + 2 * e) = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
+                            int8_t* d_out, unsigned long long* scratch, hipStream_t s) {
+  hipLaunchKernelGGL(cal_init_kernel, dim3(1), dim3(64), 0, s, scratch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t total = tokens * sh.n;
+  int64_t blocks = (total + kCalThreads - 1) / kCalThreads;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(cal_argmax_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCalThreads), 0, s,
+                     x, tokens, static_cast<int64_t>(sh.n), ld, scratch);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  H28Masks masks;
+  for (int i = 0; i < 28; ++i) masks.m[i] = h28().rowmask[i];
+  const int fill_blocks = (sh.n + 255) / 256;
+  hipLaunchKernelGGL(cal_fill_kernel, dim3(fill_blocks), dim3(256), 0, s, x, ld, sh.n, sh.k,
+                     sh.m28 ? 1 : 0, masks, scratch, d_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens,
+                          int n, float* y, hipStream_t s) {
+  const int64_t total = tokens * (n / 2);
+  int64_t blocks = (total + 255) / 256;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+  if (blocks > cap) blocks = cap;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, codes, scale,
+                     zero, tokens, n, y);
+  return hipGetLastError();
+}
+
+}  // namespace signrot

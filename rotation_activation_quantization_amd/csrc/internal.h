@@ -1,0 +1,62 @@
+// Internal declarations of libsignrot (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace signrot {
+
+// Factorisation n = m * 2^k with m in {1, 28}.
+struct Shape {
+  int n = 0;
+  int k = 0;
+  bool m28 = false;
+  bool ok = false;
+};
+Shape factor_n(int64_t n);
+
+// The library's order-28 Hadamard matrix (Paley construction I over GF(27)),
+// built once on the host.  rowmask[a] has bit a' set iff H28[a][a'] == -1.
+struct H28Table {
+  int8_t h[28][28];
+  uint32_t rowmask[28];
+};
+const H28Table& h28();
+
+// H28 row masks by value (a kernel argument).
+struct H28Masks {
+  uint32_t m[28];
+};
+
+// Everything a rotate+quant kernel needs, passed by value as the kernel
+// argument block.
+struct RqArgs {
+  const uint16_t* x;   // bf16 bits, [tokens][ld]
+  const int8_t* d;     // [n], +-1
+  uint8_t* codes;      // [tokens][n/2]
+  float* scale;        // [tokens]
+  float* zero;         // [tokens]
+  float* yout;         // [tokens][n] or nullptr
+  int64_t tokens;
+  int64_t ld;
+  int n;
+  int k;
+  int m28;
+  float inv_sqrt_n;    // binary32(1 / sqrt(n))
+  float inv_15sqrt_n;  // binary32(1 / (15 sqrt(n)))
+  uint32_t h28mask[28];
+};
+
+// Launchers; each returns the hipError_t of the launch.
+hipError_t launch_rq_generic(const RqArgs& a, hipStream_t s);
+const char* rq_generic_name();
+
+hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
+                            int8_t* d_out, unsigned long long* scratch, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float* zero,
+                          int64_t tokens, int n, float* y, hipStream_t s);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace signrot

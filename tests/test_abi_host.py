@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI: no GPU needed.  The library must load, export
+every function include/signrot.h declares, reject bad arguments before any
+HIP call, and carry an order-28 Hadamard factor equal to the oracle's (the
+two are built independently: C++ in the library, numpy in the oracle)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import rotation_activation_quantization_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "signrot.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(signrot_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return R.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 8
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(R.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True, text=True).stdout
+    for name in names:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_supported_n_table(L):
+    good = [2 ** k for k in range(1, 16)] + [28 * 2 ** k for k in range(0, 11)]
+    for n in good:
+        assert L.signrot_supported_n(n) == 1, n
+    for n in [0, 1, -4, 3, 6, 12, 14, 20, 11008, 65536, 28 * 2048, 28 * 3, 100]:
+        assert L.signrot_supported_n(n) == 0, n
+
+
+def test_library_h28_equals_oracle_h28():
+    assert np.array_equal(np.array(R.debug_h28(), dtype=np.int8), O.paley28())
+
+
+def test_strerror_texts(L):
+    for s in (0, -1, -2, -3, 7):
+        assert L.signrot_strerror(s)
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def _rq(L, x=FAKE, t=4, n=4096, ld=4096, d=FAKE, codes=FAKE, scale=FAKE, zero=FAKE, y=None):
+    return L.signrot_rotate_quant_int4(x, t, n, ld, d, codes, scale, zero, y, None)
+
+
+def test_rotate_quant_argument_errors(L):
+    assert _rq(L, n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert _rq(L, n=11008) == R.SIGNROT_EUNSUPPORTED_N
+    assert "unsupported" in L.signrot_last_error().decode()
+    assert _rq(L, t=-1) == R.SIGNROT_EINVAL
+    assert _rq(L, ld=4095) == R.SIGNROT_EINVAL
+    assert _rq(L, ld=4100) == R.SIGNROT_EINVAL  # not a multiple of 8
+    assert _rq(L, x=None) == R.SIGNROT_EINVAL
+    assert _rq(L, d=None) == R.SIGNROT_EINVAL
+    assert _rq(L, codes=None) == R.SIGNROT_EINVAL
+    assert _rq(L, scale=None) == R.SIGNROT_EINVAL
+    assert _rq(L, zero=None) == R.SIGNROT_EINVAL
+    assert _rq(L, x=FAKE + 8) == R.SIGNROT_EINVAL  # misaligned
+    assert "aligned" in L.signrot_last_error().decode()
+    # zero tokens: a no-op that succeeds even with null pointers
+    assert _rq(L, t=0, x=None, d=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK
+
+
+def test_calibrate_argument_errors(L):
+    def cal(x=FAKE, t=4, n=4096, ld=4096, d=FAKE):
+        return L.signrot_calibrate(x, t, n, ld, d, None, None, None, None)
+
+    assert cal(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert cal(t=0) == R.SIGNROT_EINVAL
+    assert cal(t=1 << 28) == R.SIGNROT_EINVAL
+    assert cal(x=None) == R.SIGNROT_EINVAL
+    assert cal(d=None) == R.SIGNROT_EINVAL
+    assert cal(ld=100) == R.SIGNROT_EINVAL
+    assert cal(x=FAKE + 2) == R.SIGNROT_EINVAL
+
+
+def test_dequant_argument_errors(L):
+    def dq(c=FAKE, s=FAKE, z=FAKE, t=3, n=4096, y=FAKE):
+        return L.signrot_dequant(c, s, z, t, n, y, None)
+
+    assert dq(n=30) == R.SIGNROT_EUNSUPPORTED_N
+    assert dq(t=-2) == R.SIGNROT_EINVAL
+    assert dq(c=None) == R.SIGNROT_EINVAL
+    assert dq(y=FAKE + 4) == R.SIGNROT_EINVAL
+    assert dq(t=0, c=None, s=None, z=None, y=None) == R.SIGNROT_OK
+
+
+def test_debug_h28_null(L):
+    assert L.signrot_debug_h28(None) == R.SIGNROT_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(R, "_lib", None)
+    monkeypatch.setattr(R, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        R.lib()

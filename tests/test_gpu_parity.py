@@ -1,0 +1,238 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every case draws its inputs from signrot_workloads or from seeded random rows,
+runs them through libsignrot on the GPU and compares with the oracle on the
+same bf16 bits (tolerances in parity.py).  Full-size workloads run every token
+on the GPU in the same launch configuration the benchmark times and compare a
+seeded sample of rows one by one; properties that hold at any size are
+checked on every row.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import rotation_activation_quantization_amd as R  # noqa: E402
+import signrot_workloads as W  # noqa: E402
+from parity import compare, expected  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(bits: np.ndarray, ld: int | None = None):
+    t, n = bits.shape
+    if ld is None:
+        ld = (n + 7) // 8 * 8
+    buf = np.zeros((max(t, 1), ld), np.uint16)
+    buf[:t, :n] = bits
+    x = torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)
+    return x[:t, :n]
+
+
+def run(bits, d_np, y_out=True, ld=None):
+    x = to_dev(bits, ld)
+    d = torch.from_numpy(np.ascontiguousarray(d_np, dtype=np.int8)).cuda()
+    out = R.rotate_quant_int4(x, d, y_out=y_out)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() if o is not None else None for o in out]
+
+
+def check_rows(bits, d_np, label, ld=None):
+    say(f"[gpu] {label}: T={bits.shape[0]} n={bits.shape[1]} kernel={R.kernel_name(bits.shape[1])}")
+    codes, scale, zero, y = run(bits, d_np, y_out=True, ld=ld)
+    st = compare(expected(bits, d_np), codes, scale, zero, y, label=label)
+    say(f"[gpu] {label}: {st}")
+    return st
+
+
+def random_d(n, seed):
+    return np.where(np.random.default_rng([7, n, seed]).random(n) < 0.5, -1, 1).astype(np.int8)
+
+
+# --------------------------------------------------------------------------
+# calibration
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3", "cfg4"])
+def test_calibrate_bit_exact(name):
+    cal_bits, meta = W.calibration_batch(name)
+    say(f"[gpu] calibrate {name} T={cal_bits.shape[0]} n={cal_bits.shape[1]}")
+    d, c, t, m = R.calibrate(to_dev(cal_bits))
+    ref = O.calibrate(cal_bits)
+    assert (c, t, m) == (ref["c"], ref["t"], np.float32(ref["m_c"]))
+    assert np.array_equal(d.cpu().numpy(), ref["d"])
+    assert c == meta["channel"]
+
+
+def test_calibrate_ties_signs_and_zero_batch():
+    x = np.zeros((3, 64), np.float32)
+    x[2, 40] = -8.0
+    x[1, 9] = 8.0
+    x[2, 9] = -8.0
+    cases = [x, -x, np.zeros((2, 64), np.float32)]
+    bits = [W.f32_to_bf16_bits(v) for v in cases]
+    negzero = np.zeros((2, 64), np.uint16)
+    negzero[1, 5] = 0x8000
+    bits.append(negzero)
+    rng = np.random.default_rng(21)
+    for _ in range(5):
+        bits.append(W.f32_to_bf16_bits(rng.integers(-3, 4, size=(5, 56)).astype(np.float32)))
+    for b in bits:
+        d, c, t, m = R.calibrate(to_dev(b))
+        ref = O.calibrate(b)
+        assert (c, t, m) == (ref["c"], ref["t"], np.float32(ref["m_c"])), (c, t, m, ref)
+        assert np.array_equal(d.cpu().numpy(), ref["d"])
+
+
+# --------------------------------------------------------------------------
+# rotate + quant: small shapes, several tiles and a ragged tail
+# --------------------------------------------------------------------------
+
+SHAPES = [2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768,
+          28, 56, 112, 224, 448, 896, 1792, 3584, 7168, 14336, 28672]
+
+
+@pytest.mark.parametrize("n", SHAPES)
+def test_rotate_quant_shapes_structured_and_random_d(n):
+    t = 37
+    bits = W.random_rows(t, n, seed=n, scale=1.0)
+    # plant a massive outlier in a third of the rows
+    c = (n * 7 // 11) % n
+    big = W.f32_to_bf16_bits(np.array([900.0], np.float32))[0]
+    bits[::3, c] = big
+    d_sr = O.calibrate(bits)["d"]
+    check_rows(bits, d_sr, f"n={n} signrot-d")
+    check_rows(bits, random_d(n, 1), f"n={n} random-d")
+    check_rows(bits, np.ones(n, np.int8), f"n={n} plain-hadamard")
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+
+_cache = {}
+
+
+def _workload(name):
+    if name not in _cache:
+        bits, meta = W.batch(name)
+        cal = O.calibrate(W.calibration_batch(name)[0])
+        _cache.clear()
+        _cache[name] = (bits, meta, cal)
+    return _cache[name]
+
+
+@pytest.mark.parametrize("name,sample", [("cfg1", None), ("cfg2", None), ("cfg3", 192),
+                                         ("target", 96), ("cfg4", 40)])
+def test_workload_parity(name, sample):
+    bits, meta, cal = _workload(name)
+    t, n = bits.shape
+    say(f"[gpu] workload {name}: T={t} n={n} kernel={R.kernel_name(n)} sample={sample}")
+    x = to_dev(bits)
+    d = torch.from_numpy(cal["d"]).cuda()
+    codes, scale, zero, y = R.rotate_quant_int4(x, d, y_out=True)
+    torch.cuda.synchronize()
+    if sample is None:
+        rows = np.arange(t)
+    else:
+        g = np.random.default_rng([5, t, n])
+        outl = meta["outlier_tokens"]
+        rows = np.unique(np.concatenate([g.choice(t, sample // 2, replace=False),
+                                         g.choice(outl, sample - sample // 2, replace=False),
+                                         [0, t - 1]]))
+    idx = torch.from_numpy(rows).cuda()
+    st = compare(expected(bits[rows], cal["d"]), codes[idx].cpu().numpy(), scale[idx].cpu().numpy(),
+                 zero[idx].cpu().numpy(), y[idx].cpu().numpy(), label=name)
+    say(f"[gpu] {name} rows={len(rows)}: {st}")
+    # properties on every row: the extremes map to codes 0 and 15
+    q = O.unpack_int4(codes.cpu().numpy())
+    assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == 15)
+    assert np.all(scale.cpu().numpy() > 0)
+    # without y_out the codes are identical
+    c2, s2, z2 = R.rotate_quant_int4(x, d, y_out=False)
+    torch.cuda.synchronize()
+    assert torch.equal(c2, codes) and torch.equal(s2, scale) and torch.equal(z2, zero)
+
+
+def test_decode_batches():
+    cal = O.calibrate(W.calibration_batch("cfg5")[0])
+    d = cal["d"]
+    for batch, reps in ((1, 100), (4, 25), (16, 8)):
+        say(f"[gpu] decode batch={batch} reps={reps}")
+        allb, allc, alls, allz, ally = [], [], [], [], []
+        for r in range(reps):
+            bits, _ = W.decode_batch("cfg5", batch, r)
+            codes, scale, zero, y = run(bits, d)
+            allb.append(bits); allc.append(codes); alls.append(scale); allz.append(zero); ally.append(y)
+        compare(expected(np.concatenate(allb), d), np.concatenate(allc), np.concatenate(alls),
+                np.concatenate(allz), np.concatenate(ally), label=f"decode{batch}")
+
+
+def test_no_outlier_control_batch():
+    bits, _ = W.control_batch("cfg5", tokens=256)
+    cal = O.calibrate(W.calibration_batch("cfg5")[0])
+    check_rows(bits, cal["d"], "control")
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n", [4096, 14336, 28, 2])
+def test_degenerate_rows(n):
+    c = n // 3
+    rows = np.zeros((6, n), np.uint16)
+    rows[1, :] = W.f32_to_bf16_bits(np.full(n, 2.5, np.float32))  # constant input
+    rows[2, c] = W.f32_to_bf16_bits(np.array([1512.0], np.float32))[0]  # lone outlier
+    rows[3, c] = W.f32_to_bf16_bits(np.array([-640.0], np.float32))[0]
+    rows[4, ::2] = 0x8000  # -0.0
+    rows[5] = W.random_rows(1, n, seed=3, scale=1e-3)[0]
+    d = O.calibrate(rows[2:3])["d"]
+    st = check_rows(rows, d, f"degenerate n={n}")
+    codes, scale, zero, y = run(rows, d)
+    assert scale[0] == 1.0 and np.all(codes[0] == 0)  # all-zero row
+    assert scale[2] == 1.0 and np.all(codes[2] == 0)  # lone outlier after the flip
+    assert st["code_mismatches"] == 0
+
+
+def test_strided_rows_and_ragged_token_counts():
+    n = 14336
+    for t in (1, 3, 255, 257, 1031):
+        bits = W.random_rows(t, n, seed=t, scale=0.7, outlier=1200.0)
+        d = O.calibrate(bits)["d"]
+        check_rows(bits, d, f"ragged T={t}", ld=n + 64)
+
+
+def test_zero_tokens_is_noop():
+    x = torch.empty((0, 4096), dtype=torch.bfloat16, device="cuda")
+    d = torch.ones(4096, dtype=torch.int8, device="cuda")
+    codes, scale, zero = R.rotate_quant_int4(x, d)
+    assert codes.shape == (0, 2048)
+
+
+def test_dequant_matches_oracle():
+    bits, _ = W.batch("cfg1")
+    cal = O.calibrate(bits)
+    y = O.rotate(O.bf16_bits_to_f64(bits), cal["d"])
+    q, s, z = O.quant_asym(y)
+    packed = O.pack_int4(q)
+    s32, z32 = s.astype(np.float32), z.astype(np.float32)
+    yh = R.dequant(torch.from_numpy(packed).cuda(), torch.from_numpy(s32).cuda(), torch.from_numpy(z32).cuda())
+    torch.cuda.synchronize()
+    ref = O.dequant(q, s32.astype(np.float64), z32.astype(np.float64))
+    err = np.abs(yh.cpu().numpy() - ref) / np.abs(ref).max(axis=1, keepdims=True)
+    assert err.max() < 1e-6
+    # quantization error of the round trip is at most half a step
+    assert np.all(np.abs(yh.cpu().numpy() - y) <= s[:, None] * 0.5 * (1 + 1e-5) + 1e-6)
