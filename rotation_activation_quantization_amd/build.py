@@ -18,6 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = [
     "api.hip",
     "rq_generic.hip",
+    "rq_mfma.hip",
     "calib_dequant.hip",
     "hadamard28.cpp",
 ]
@@ -33,6 +34,8 @@ COMMON = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs (the VALU reads them right away)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 
