@@ -80,4 +80,87 @@ __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, in
   return f;
 }
 
+// Sign bits (bit set when the byte is negative) of 32 consecutive int8
+// entries d[32 w .. 32 w + 31], read as two 16-byte loads.
+__device__ __forceinline__ uint32_t sign_word(const int8_t* d32) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(d32);
+  const uint4 hi = *reinterpret_cast<const uint4*>(d32 + 16);
+  const uint32_t q[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t word = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t s = (q[i] >> 7) & 0x01010101u;  // one sign per byte at bits 0, 8, 16, 24
+    const uint32_t nib = (s | (s >> 7) | (s >> 14) | (s >> 21)) & 0xfu;
+    word |= nib << (4 * i);
+  }
+  return word;
+}
+
+// Builds the d bitmask in LDS (n / 32 words; needs n % 32 == 0 and d 16-byte
+// aligned) with every thread of the block.
+__device__ inline void build_dbits(const int8_t* d, int n, uint32_t* dbits) {
+  for (int w = threadIdx.x; w < n / 32; w += blockDim.x) dbits[w] = sign_word(d + 32 * w);
+}
+
+// Same decision as decode_d_form, in parallel, for k >= 5 (a 32-bit word of
+// the mask then lies inside one block of 2^k channels).  h28 holds the row
+// masks of H28 in LDS.  Every thread of the block must call it.
+__device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbits, const uint32_t* h28,
+                                           int* sh_scratch) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  auto dbit = [&](int j) -> uint32_t { return (dbits[j >> 5] >> (j & 31)) & 1u; };
+  if (tid < 64) {
+    const uint32_t d0 = dbit(0);
+    // bit t of c_b: sign change between b = 0 and b = 2^t (first block)
+    const unsigned long long cbm = __ballot(lane < a.k && dbit(1 << lane) != d0);
+    const int cb = static_cast<int>(cbm & ((1ull << a.k) - 1ull));
+    int ca = 0, found = 1;
+    if (a.m28) {
+      // normalised first column of each block against each normalised H28 row
+      const unsigned long long em = __ballot(lane < 28 && (dbit(lane << a.k) ^ d0) != 0u);
+      const uint32_t e = static_cast<uint32_t>(em);
+      uint32_t norm = 0xffffffffu;
+      if (lane < 28) {
+        const uint32_t m = h28[lane];
+        norm = (m & 1u) ? (~m & 0x0fffffffu) : m;
+      }
+      const unsigned long long hit = __ballot(lane < 28 && norm == e);
+      found = hit != 0ull;
+      ca = found ? __builtin_ctzll(hit) : 0;
+    }
+    if (tid == 0) {
+      sh_scratch[0] = found;
+      sh_scratch[1] = (ca << a.k) | cb;
+      sh_scratch[2] = static_cast<int>(d0 ^ (a.m28 ? (h28[ca] & 1u) : 0u));
+    }
+  }
+  __syncthreads();
+  DForm f{sh_scratch[0], sh_scratch[1], sh_scratch[2]};
+  int bad = 0;
+  if (f.structured) {
+    const int bmask = (1 << a.k) - 1;
+    const int cb = f.c & bmask;
+    const int ca = f.c >> a.k;
+    // parity(cb & i) for i = 0..31, as a word
+    uint32_t pw = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) pw |= (__popc(static_cast<uint32_t>(cb & i)) & 1u) << i;
+    for (int w = tid; w < a.n / 32; w += blockDim.x) {
+      const int j0 = 32 * w;
+      uint32_t flip = static_cast<uint32_t>(f.neg) ^ (__popc(static_cast<uint32_t>(cb & j0 & bmask)) & 1u);
+      if (a.m28) flip ^= (h28[ca] >> (j0 >> a.k)) & 1u;
+      const uint32_t want = flip ? ~pw : pw;
+      bad |= static_cast<int>(dbits[w] != want);
+    }
+  }
+  bad = __syncthreads_or(bad);
+  if (bad) f.structured = 0;
+  if (!f.structured) {
+    f.c = -1;
+    f.neg = 0;
+  }
+  return f;
+}
+
 }  // namespace signrot
