@@ -318,22 +318,32 @@ __device__ void rq_mfma_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     lds_barrier();
     const float xc = GENERAL ? 0.0f : xc_lds[0];
 
-    // (2) MFMA stage: gather the data operand (dwords = bf16 pairs) and multiply
+    // (2) MFMA stage: gather the data operand (dwords = bf16 pairs) and
+    // multiply; the gathers of tile t+1 are issued before the MFMAs of tile t.
     float v[NV];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    auto gather = [&](int t, u32x4_t& w0, u32x4_t& w1) {
       const uint8_t* base = lds + gaddr[t];
-      u32x4_t w0, w1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         w0[j] = *reinterpret_cast<const uint32_t*>(base + (4 * j) * PITCH);
         w1[j] = (16 + 4 * j < KA) ? *reinterpret_cast<const uint32_t*>(base + (16 + 4 * j) * PITCH) : 0u;
       }
+    };
+    u32x4_t cw0, cw1;
+    gather(0, cw0, cw1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      u32x4_t nw0, nw1;
+      if (t + 1 < NT) gather(t + 1, nw0, nw1);
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[0], __builtin_bit_cast(bf16x8_t, w0), acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[1], __builtin_bit_cast(bf16x8_t, w1), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[0], __builtin_bit_cast(bf16x8_t, cw0), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[1], __builtin_bit_cast(bf16x8_t, cw1), acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[t * 4 + r] = acc[r];
+      if (t + 1 < NT) {
+        cw0 = nw0;
+        cw1 = nw1;
+      }
     }
     // (3) every wave has read the row buffer: start the next row's DMA
     lds_barrier();
