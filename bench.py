@@ -36,6 +36,41 @@ sys.path.insert(0, HERE)
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
 WORKLOAD = "target"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
+# Sources that define the timed kernel; the HBM traffic measured with
+# rocprofv3 counters is reported only while they are unchanged.
+KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_mfma.hip",
+                  "rotation_activation_quantization_amd/csrc/device_common.h",
+                  "rotation_activation_quantization_amd/csrc/internal.h",
+                  "rotation_activation_quantization_amd/build.py")
+TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(HERE, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, n: int, t: int):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for a plain copy of
+    known size), or None if there is none or the kernel has changed since."""
+    path = os.path.join(HERE, TRAFFIC_PROFILE.format(kernel=kernel, n=n, t=t))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for ln in f:
+            if "=" in ln and not ln.startswith("#"):
+                k, v = ln.strip().split("=", 1)
+                kv[k] = v
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
 
 
 def algorithmic_bytes_per_token(n: int) -> int:
@@ -128,17 +163,19 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # per-launch HIP events on the stream the kernel runs on
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # HIP events over the whole timed region, recorded on the stream the
+    # kernel is launched on; average launch duration = elapsed / steps
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        evs[i][0].record(stream)
         step(i)
-        evs[i][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
 
     if args.pmc_copy:
         # plain copies of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
@@ -152,8 +189,10 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     tokens_per_s = t * args.steps / wall
     bpt = algorithmic_bytes_per_token(n)
-    avg_kernel_ms = float(kern_ms.mean())
     achieved = bpt * t / (avg_kernel_ms * 1e-3) / 1e9
+    kname = R.kernel_name(n)
+    traffic_bytes = measured_traffic(kname, n, t)
+    traffic = None if traffic_bytes is None else traffic_bytes / (avg_kernel_ms * 1e-3) / 1e9
     line = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak), fused SignRot rotate+INT4 quant",
         "value": tokens_per_s,
@@ -174,11 +213,10 @@ def main() -> int:
             "n": n,
             "tokens": t,
             "parallelism": "single GPU",
-            "kernel": R.kernel_name(n),
+            "kernel": kname,
             "input_buffer_sets": nsets,
             "hbm_gbs_wall": bpt * tokens_per_s / 1e9,
             "pct_of_peak_hbm_wall": 100.0 * bpt * tokens_per_s / 1e9 / PEAK_HBM_GBS,
-            "kernel_ms_p10_p50_p90": [float(np.percentile(kern_ms, q)) for q in (10, 50, 90)],
         },
         "roofline": {
             "bound": "hbm",
@@ -186,7 +224,9 @@ def main() -> int:
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_bytes_per_launch": traffic_bytes,
+            "algorithmic_bytes_per_launch": bpt * t,
             "bytes_per_token": bpt,
             "kernel_avg_ms": avg_kernel_ms,
         },
