@@ -92,18 +92,23 @@ int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
  *   q_j   = clamp(round((y_j - mn) / scale), 0, 15), round to nearest.
  *
  *   x_bf16  device, [tokens][ld] bf16.
- *   d       device, [n] int8, every entry +1 or -1 (any other value gives
- *           unspecified output).  When d = sigma * (row c of H) -- the form
+ *   d       device, [n] int8, 16-byte aligned, every entry +1 or -1 (any
+ *           other value gives unspecified output).  When d = sigma * (row c of H) -- the form
  *           signrot_calibrate produces -- the library recognises it and
  *           evaluates the identical quantity as ((x - x_c e_c) . H) (.) d plus
  *           the constant sigma * x_c / sqrt(n), so the outlier is added once
  *           instead of being rounded through every butterfly stage.
- *   codes   device, [tokens][n/2] uint8: code of channel 2m in the low nibble
- *           of byte m, channel 2m+1 in the high nibble.
+ *   codes   device, [tokens][n/2] uint8, 16-byte aligned: code of channel 2m
+ *           in the low nibble of byte m, channel 2m+1 in the high nibble.
  *   scale   device, [tokens] float.
  *   zero    device, [tokens] float.
- *   y_out   device, [tokens][n] float, or NULL: the rotated, flipped values
- *           in binary32 (a debugging output; the codes do not depend on it).
+ *   y_out   device, [tokens][n] float, 16-byte aligned, or NULL: the
+ *           rotated, flipped values in binary32 (a debugging output; the
+ *           codes do not depend on it).
+ *
+ * A misaligned x, d, codes or y_out, ld < n or ld not a multiple of 8, a null
+ * pointer (tokens > 0) or tokens < 0 -> SIGNROT_EINVAL; an unsupported n ->
+ * SIGNROT_EUNSUPPORTED_N.
  *
  * Asynchronous: returns once the kernel is enqueued on `stream`.  Arithmetic
  * is binary32 throughout.

@@ -158,6 +158,9 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   if (tokens > (int64_t{1} << 40)) return fail_einval("tokens too large");
   if (!x_bf16 || !d || !codes || !scale || !zero) return fail_einval("null device pointer");
   if (!aligned16(x_bf16)) return fail_einval("x must be 16-byte aligned");
+  if (!aligned16(d)) return fail_einval("d must be 16-byte aligned");
+  if (!aligned16(codes)) return fail_einval("codes must be 16-byte aligned");
+  if (y_out && !aligned16(y_out)) return fail_einval("y_out must be 16-byte aligned");
   RqArgs a;
   memset(&a, 0, sizeof(a));
   a.x = static_cast<const uint16_t*>(x_bf16);

@@ -78,6 +78,9 @@ def test_rotate_quant_argument_errors(L):
     assert _rq(L, zero=None) == R.SIGNROT_EINVAL
     assert _rq(L, x=FAKE + 8) == R.SIGNROT_EINVAL  # misaligned
     assert "aligned" in L.signrot_last_error().decode()
+    assert _rq(L, d=FAKE + 4) == R.SIGNROT_EINVAL  # d is read 16 bytes at a time
+    assert _rq(L, codes=FAKE + 8) == R.SIGNROT_EINVAL  # codes are stored 16 bytes at a time
+    assert _rq(L, y=FAKE + 4) == R.SIGNROT_EINVAL
     # zero tokens: a no-op that succeeds even with null pointers
     assert _rq(L, t=0, x=None, d=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK
 
