@@ -236,3 +236,29 @@ def test_dequant_matches_oracle():
     assert err.max() < 1e-6
     # quantization error of the round trip is at most half a step
     assert np.all(np.abs(yh.cpu().numpy() - y) <= s[:, None] * 0.5 * (1 + 1e-5) + 1e-6)
+
+
+def test_gpu_round_trip_mse_matches_oracle():
+    """End to end on the GPU (rotate + quantize, then dequant) the per-token
+    quantization MSE of SignRot + asymmetric INT4 equals the oracle's, and on
+    outlier tokens it is far below plain Hadamard + symmetric INT4."""
+    bits, meta = W.batch("cfg3", tokens=64)
+    d_np = O.calibrate(W.calibration_batch("cfg3")[0])["d"]
+    say("[gpu] round-trip MSE cfg3 T=64")
+    x = to_dev(bits)
+    codes, scale, zero = R.rotate_quant_int4(x, torch.from_numpy(d_np).cuda())
+    yh = R.dequant(codes, scale, zero)
+    torch.cuda.synchronize()
+    xf = O.bf16_bits_to_f64(bits)
+    y = O.rotate(xf, d_np)
+    m_gpu = O.mse(y, yh.cpu().numpy())
+    q, s, z = O.quant_asym(y)
+    m_or = O.mse(y, O.dequant(q, s, z))
+    assert np.all(np.abs(m_gpu - m_or) <= 1e-3 * m_or)
+    out = meta["outlier_tokens"][meta["outlier_tokens"] < 64]
+    assert len(out) > 0
+    yp = O.rotate(xf)
+    qs, ss = O.quant_sym(yp)
+    m_ps = O.mse(yp, O.dequant_sym(qs, ss))
+    assert np.all(m_gpu[out] * 10 < m_ps[out])
+    say(f"[gpu] MSE outlier tokens gpu={m_gpu[out].mean():.5f} plain_sym={m_ps[out].mean():.5f}")

@@ -442,3 +442,47 @@ def test_mse_ordering_on_outlier_and_control_tokens():
     m_sr, m_pa, m_ps = asym(y_sr), asym(y_plain), sym(y_plain)
     assert np.all(m_sr[out] < m_pa[out]) and np.all(m_sr[out] < m_ps[out])
     assert m_sr[~out].mean() < 1.1 * m_pa[~out].mean()
+
+
+def _mse_grid():
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "mse_grid.json")) as f:
+        return json.load(f)
+
+
+def test_mse_grid_directions():
+    """Stored MSE grid (written by tests/golden/make_mse_grid.py from the oracle):
+    the flip leaves the symmetric quantizer unchanged on every workload; on
+    outlier tokens SignRot + asymmetric INT4 cuts the error of both plain
+    quantizers by more than 10x; without an outlier it matches plain + asym."""
+    g = _mse_grid()["workloads"]
+    assert set(g) == {"cfg1", "cfg2", "cfg3", "cfg4", "cfg5_control"}
+    for name, w in g.items():
+        for part in ("outlier", "no_outlier"):
+            if part not in w:
+                continue
+            c = w[part]
+            assert c["signrot_sym"] == c["plain_sym"], (name, part)
+            if part == "outlier":
+                assert c["tokens"] > 0
+                assert c["signrot_asym"] * 10 < c["plain_asym"] < c["plain_sym"], (name, c)
+            else:
+                assert abs(c["signrot_asym"] - c["plain_asym"]) < 0.05 * c["plain_asym"], (name, c)
+
+
+def test_mse_grid_is_the_oracles():
+    """The stored cfg1 cells are what the oracle computes now."""
+    g = _mse_grid()["workloads"]["cfg1"]
+    bits, meta = W.batch("cfg1")
+    d = O.calibrate(W.calibration_batch("cfg1")[0])["d"]
+    x = O.bf16_bits_to_f64(bits)
+    y_sr = O.rotate(x, d)
+    q, s, z = O.quant_asym(y_sr)
+    m = O.mse(y_sr, O.dequant(q, s, z))
+    has = np.zeros(len(x), bool)
+    has[meta["outlier_tokens"]] = True
+    assert g["outlier"]["tokens"] == int(has.sum())
+    assert abs(m[has].mean() - g["outlier"]["signrot_asym"]) <= 1e-12 * g["outlier"]["signrot_asym"]
+    assert abs(m[~has].mean() - g["no_outlier"]["signrot_asym"]) <= 1e-12 * g["no_outlier"]["signrot_asym"]
