@@ -15,8 +15,9 @@ The inputs are copied to several device buffers whose total exceeds the
 step reads its input from HBM.
 
 Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
---warmup W, --no-cpu-baseline, --pmc-copy (also run plain copies of known size
-for the counter calibration of a rocprofv3 --pmc run).
+--warmup W, --no-cpu-baseline, --no-decode (skip the decode-latency leg),
+--pmc-copy (also run plain copies of known size for the counter calibration
+of a rocprofv3 --pmc run).
 """
 
 from __future__ import annotations
@@ -38,7 +39,8 @@ WORKLOAD = "target"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # Sources that define the timed kernel; the HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
-KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_mfma.hip",
+KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_w7.hip",
+                  "rotation_activation_quantization_amd/csrc/wave_ops.h",
                   "rotation_activation_quantization_amd/csrc/device_common.h",
                   "rotation_activation_quantization_amd/csrc/internal.h",
                   "rotation_activation_quantization_amd/build.py")
@@ -107,14 +109,75 @@ def cpu_baseline(bits: np.ndarray, d: np.ndarray, budget_s: float = 12.0) -> dic
                       f"oracle rotate (float64 blocked dense product) + asymmetric INT4, {dt:.1f} s"}
 
 
+def decode_latency(R, W, torch, d, calls: int = 10000) -> dict:
+    """Latency of decode-shaped calls (1, 4, 16 tokens of the n = 14336 law):
+    microseconds per call for back-to-back launches and for one HIP graph
+    holding `calls` launches.  The graph's output is checked against an eager
+    call on the same input after every replay."""
+    out = {}
+    fn = R.lib().signrot_rotate_quant_int4
+    for t in (1, 4, 16):
+        bits, _ = W.decode_batch("cfg5", t, 0)
+        n = bits.shape[1]
+        x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        co = torch.empty((t, n // 2), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(t, dtype=torch.float32, device="cuda")
+        ze = torch.empty(t, dtype=torch.float32, device="cuda")
+        ref = R.rotate_quant_int4(x, d)
+
+        def launch(stream):
+            st = fn(x.data_ptr(), t, n, n, d.data_ptr(), co.data_ptr(), sc.data_ptr(), ze.data_ptr(), None,
+                    ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                R.check(st, "signrot_rotate_quant_int4")
+
+        stream = torch.cuda.current_stream()
+        for _ in range(100):
+            launch(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(calls):
+            launch(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_launch = e0.elapsed_time(e1) * 1e3 / calls
+
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                cap = torch.cuda.current_stream()
+                for _ in range(calls):
+                    launch(cap)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        times = []
+        for rep in range(3):
+            co.zero_()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / calls)
+            if not (torch.equal(co, ref[0]) and torch.equal(sc, ref[1]) and torch.equal(ze, ref[2])):
+                raise RuntimeError(f"graph replay {rep} differs from the eager call at {t} tokens")
+        del g
+        out[str(t)] = {"us_per_call_launch": us_launch, "us_per_call_graph": float(np.median(times))}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); "
@@ -231,6 +294,9 @@ def main() -> int:
             "kernel_avg_ms": avg_kernel_ms,
         },
     }
+    if not args.no_decode:
+        line["decode"] = {"workload": "n=14336, 1/4/16 tokens per call, same law; 10^4 calls",
+                          "tokens": decode_latency(R, W, torch, d)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy())
     print(json.dumps(line), flush=True)

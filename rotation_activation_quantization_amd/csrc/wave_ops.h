@@ -1,0 +1,196 @@
+// Wave-level building blocks shared by the MFMA rotate+quant kernels (gfx950):
+// operand vector types, the DPP butterfly stages of the 16-point lane
+// transform, in-register butterflies, min/max helpers and wave reductions,
+// and the LDS-only barrier.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace signrot {
+namespace wave {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+// The four DPP stages below (masks 1, 2, 7, 8 with the sign selectors
+// gdpp0..3 of the kernels) compute the 16-point Walsh-Hadamard transform of
+// the values held by the lanes of a 16-lane row when lane nl starts with the
+// input of index nl ^ kXLane; the output of index lane_perm(nl) ends in lane nl.
+constexpr int kXLane = 12;
+
+// Output pair-lane index of lane n after the four DPP stages (a linear map on
+// the 4 lane bits): bit 0 -> 5, bit 1 -> 6, bit 2 -> 7, bit 3 -> 8.
+__device__ __forceinline__ int lane_perm(int nl) {
+  int r = (nl & 8);
+  if (nl & 1) r ^= 5;
+  if (nl & 2) r ^= 6;
+  if (nl & 4) r ^= 7;
+  return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_of_sign(int s) {
+  return s > 0 ? 0x3f80u : (s < 0 ? 0xbf80u : 0u);
+}
+
+template <int KA>
+__device__ __forceinline__ int hka_sign(const uint32_t* h28, int row, int col) {
+  if (KA == 28) return ((h28[row] >> col) & 1u) ? -1 : 1;
+  return (__popc(static_cast<uint32_t>(row & col)) & 1) ? -1 : 1;
+}
+
+// One DPP butterfly stage on 16 registers: v += g * v[lane ^ m] (m given by
+// the DPP control).  The leading s_nop covers the VALU-write -> DPP-read hazard
+// for whatever instruction preceded the block; inside the block every
+// instruction reads and writes its own register.
+#define SR_DPP16(CTRL, R, G)                                                              \
+  asm volatile("s_nop 1\n"                                                               \
+               "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"        \
+               "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf\n"      \
+               : "+v"(R[0]), "+v"(R[1]), "+v"(R[2]), "+v"(R[3]), "+v"(R[4]), "+v"(R[5]),   \
+                 "+v"(R[6]), "+v"(R[7]), "+v"(R[8]), "+v"(R[9]), "+v"(R[10]), "+v"(R[11]), \
+                 "+v"(R[12]), "+v"(R[13]), "+v"(R[14]), "+v"(R[15])                        \
+               : "v"(G))
+
+template <int NV>
+__device__ __forceinline__ void dpp_stage(float (&v)[NV], float g, int which) {
+  static_assert(NV % 16 == 0, "registers in blocks of 16");
+#pragma unroll
+  for (int b = 0; b < NV; b += 16) {
+    float* R = v + b;
+    if (which == 0) SR_DPP16("quad_perm:[1,0,3,2]", R, g);
+    else if (which == 1) SR_DPP16("quad_perm:[2,3,0,1]", R, g);
+    else if (which == 2) SR_DPP16("row_half_mirror", R, g);
+    else SR_DPP16("row_ror:8", R, g);
+  }
+}
+
+// In-register butterflies (p, q) -> (p + q, p - q) over tile bit U of the
+// value array v[t * 4 + r].
+template <int NT, int U>
+__device__ __forceinline__ void reg_stage(float (&v)[NT * 4]) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    if (t & (1 << U)) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float& p = v[t * 4 + r];
+      float& q = v[(t | (1 << U)) * 4 + r];
+      const float s = p + q;
+      const float dd = p - q;
+      p = s;
+      q = dd;
+    }
+  }
+}
+
+// acc = min(acc, x, y) and acc = max(acc, x, y) as single v_min3/v_max3 ops
+__device__ __forceinline__ void min3_acc(float& acc, float x, float y) {
+  asm("v_min3_f32 %0, %0, %1, %2" : "+v"(acc) : "v"(x), "v"(y));
+}
+__device__ __forceinline__ void max3_acc(float& acc, float x, float y) {
+  asm("v_max3_f32 %0, %0, %1, %2" : "+v"(acc) : "v"(x), "v"(y));
+}
+
+// Plain v_min_f32 / v_max_f32.  fminf / fmaxf make the compiler quiet NaN
+// inputs with an extra v_max_f32 x, x, x on every operand it cannot prove
+// canonical (DPP results, LDS loads); the inputs here are finite.
+__device__ __forceinline__ float fmin_raw(float x, float y) {
+  float r;
+  asm("v_min_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+__device__ __forceinline__ float fmax_raw(float x, float y) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(y));
+  return r;
+}
+
+// Wave-wide min and max, every lane gets the result: DPP inside 16-lane rows,
+// then the gfx950 row swaps across rows and halves.
+__device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
+  // inside each 16-lane row: lane ^ 1, lane ^ 2, mirror in 8, mirror in 16,
+  // each step one v_min/v_max with a DPP source; the s_nop cover the
+  // VALU-write -> DPP-read hazard of the chained registers
+  asm volatile(
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n"
+      : "+v"(mn), "+v"(mx));
+  {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mn = fmin_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    mx = fmax_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    mn = fmin_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    mx = fmax_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+}
+
+// Quantizer constants of a token from the min and max of its rotated values
+// (any common scale): inv = 15 / range through v_rcp_f32 (within 1 ulp, so a
+// code can move only for a value within ~1e-6 of a rounding boundary), the
+// offset cq = -mn * inv, and the zero-point in code units -(mn + shift) * inv
+// when the values exclude a constant shift.  A zero range gives inv = 0, all
+// codes 0.
+struct QuantParams {
+  float inv, cq, range;
+  bool degenerate;
+};
+__device__ __forceinline__ QuantParams quant_params(float mn, float mx) {
+  QuantParams q;
+  q.range = mx - mn;
+  q.degenerate = !(q.range > 0.0f);
+  q.inv = q.degenerate ? 0.0f : 15.0f * __builtin_amdgcn_rcpf(q.range);
+  q.cq = -mn * q.inv;
+  return q;
+}
+
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global loads and stores (the next row's DMA and this row's code stores stay
+// in flight); the memory clobber keeps the compiler from moving memory
+// accesses across it.  Global data that other waves read from LDS (the DMA'd
+// row) is covered by an explicit vmcnt wait before the barrier that needs it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// vmcnt(N) with expcnt and lgkmcnt left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+}  // namespace wave
+}  // namespace signrot
