@@ -39,7 +39,7 @@ WORKLOAD = "target"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # Sources that define the timed kernel; the HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
-KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_w7.hip",
+KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_fast.hip",
                   "rotation_activation_quantization_amd/csrc/wave_ops.h",
                   "rotation_activation_quantization_amd/csrc/device_common.h",
                   "rotation_activation_quantization_amd/csrc/internal.h",
@@ -107,6 +107,18 @@ def cpu_baseline(bits: np.ndarray, d: np.ndarray, budget_s: float = 12.0) -> dic
     return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} tokens of the same workload (n={bits.shape[1]}), "
                       f"oracle rotate (float64 blocked dense product) + asymmetric INT4, {dt:.1f} s"}
+
+
+def workload_text(w, n: int, t: int, c: int) -> str:
+    width = {4096: "2^12", 8192: "2^13", 14336: "28*2^9, LLaMA3-8B down_proj input",
+             28672: "28*2^10, LLaMA3-70B down_proj input"}.get(n, str(n))
+    law = f"N(0,{w.width:g})" if w.law == "normal" else f"{w.width:g}*t({w.df:g})"
+    sign = "+" if w.p_positive >= 1.0 else f"+-(+ {w.p_positive:.0%})"
+    mild = f", {w.mild_channels} mild channels x{w.mild_factor:g}" if w.mild_channels else ""
+    cal = "the batch itself" if w.calib_same else f"{w.calib_tokens} tokens"
+    return (f"n={n} ({width}) x {t} tokens bf16, {law} background{mild}, outlier channel {c} with "
+            f"{sign}M, M~U[{w.m_lo:g},{w.m_hi:g}] in {w.p_outlier:.0%} of tokens; SignRot sign vector from "
+            f"calibration on {cal}")
 
 
 def decode_latency(R, W, torch, d, calls: int = 10000) -> dict:
@@ -178,6 +190,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--workload", default=WORKLOAD, choices=["cfg1", "cfg2", "cfg3", "target", "cfg4"],
+                    help="synthetic workload to time (default: n=14336 x 8192 tokens)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); "
@@ -196,11 +210,12 @@ def main() -> int:
     torch.cuda.set_device(0)
     L = R.lib()
 
-    w = W.WORKLOADS[WORKLOAD]
-    bits, meta = W.batch(WORKLOAD, tokens=args.tokens)
+    wname = args.workload
+    w = W.WORKLOADS[wname]
+    bits, meta = W.batch(wname, tokens=args.tokens)
     t, n = bits.shape
     x0 = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    d, c, _, _ = R.calibrate(to_dev_bits(W.calibration_batch(WORKLOAD)[0], torch))
+    d, c, _, _ = R.calibrate(to_dev_bits(W.calibration_batch(wname)[0], torch))
 
     in_bytes = x0.numel() * 2
     nsets = max(2, int(np.ceil(BUFFER_SETS_MIN_BYTES / in_bytes)))
@@ -270,9 +285,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"n={n} (28*2^9, LLaMA3-8B down_proj input) x {t} tokens bf16, N(0,0.7) background, "
-                        f"outlier channel {c} with M~U[{w.m_lo:g},{w.m_hi:g}] in {w.p_outlier:.0%} of tokens; "
-                        f"SignRot sign vector from calibration on {w.calib_tokens} tokens",
+            "workload": workload_text(w, n, t, c),
             "n": n,
             "tokens": t,
             "parallelism": "single GPU",
@@ -294,7 +307,7 @@ def main() -> int:
             "kernel_avg_ms": avg_kernel_ms,
         },
     }
-    if not args.no_decode:
+    if not args.no_decode and n == 14336:
         line["decode"] = {"workload": "n=14336, 1/4/16 tokens per call, same law; 10^4 calls",
                           "tokens": decode_latency(R, W, torch, d)}
     if not args.no_cpu_baseline:

@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = [
     "api.hip",
     "rq_generic.hip",
-    "rq_w7.hip",
+    "rq_fast.hip",
     "calib_dequant.hip",
     "hadamard28.cpp",
 ]

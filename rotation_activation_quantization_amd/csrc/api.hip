@@ -104,7 +104,7 @@ int signrot_debug_h28(int8_t* out) {
 const char* signrot_kernel_name(int64_t n) {
   const Shape sh = factor_n(n);
   if (!sh.ok) return nullptr;
-  return rq_w7_supports(sh.n, sh.k, sh.m28) ? rq_w7_name() : rq_generic_name();
+  return rq_fast_supports(sh.n, sh.k, sh.m28) ? rq_fast_name(sh.n) : rq_generic_name();
 }
 
 int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
@@ -178,7 +178,7 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = rq_w7_supports(sh.n, sh.k, sh.m28) ? launch_rq_w7(a, st) : launch_rq_generic(a, st);
+  hipError_t e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, st) : launch_rq_generic(a, st);
   if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4 launch");
   return SIGNROT_OK;
 }

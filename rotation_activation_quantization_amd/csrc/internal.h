@@ -50,9 +50,9 @@ struct RqArgs {
 // Launchers; each returns the hipError_t of the launch.
 hipError_t launch_rq_generic(const RqArgs& a, hipStream_t s);
 const char* rq_generic_name();
-bool rq_w7_supports(int n, int k, bool m28);
-hipError_t launch_rq_w7(const RqArgs& a, hipStream_t s);
-const char* rq_w7_name();
+bool rq_fast_supports(int n, int k, bool m28);
+hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s);
+const char* rq_fast_name(int n);
 
 hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
                             int8_t* d_out, unsigned long long* scratch, hipStream_t s);

@@ -66,16 +66,38 @@ __device__ __forceinline__ int hka_sign(const uint32_t* h28, int row, int col) {
                  "+v"(R[12]), "+v"(R[13]), "+v"(R[14]), "+v"(R[15])                        \
                : "v"(G))
 
+// The same on 8 registers.
+#define SR_DPP8(CTRL, R, G)                                                              \
+  asm volatile("s_nop 1\n"                                                              \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"         \
+               : "+v"(R[0]), "+v"(R[1]), "+v"(R[2]), "+v"(R[3]), "+v"(R[4]), "+v"(R[5]),  \
+                 "+v"(R[6]), "+v"(R[7])                                                   \
+               : "v"(G))
+
 template <int NV>
 __device__ __forceinline__ void dpp_stage(float (&v)[NV], float g, int which) {
-  static_assert(NV % 16 == 0, "registers in blocks of 16");
+  static_assert(NV % 8 == 0, "registers in blocks of 8");
 #pragma unroll
-  for (int b = 0; b < NV; b += 16) {
+  for (int b = 0; b + 16 <= NV; b += 16) {
     float* R = v + b;
     if (which == 0) SR_DPP16("quad_perm:[1,0,3,2]", R, g);
     else if (which == 1) SR_DPP16("quad_perm:[2,3,0,1]", R, g);
     else if (which == 2) SR_DPP16("row_half_mirror", R, g);
     else SR_DPP16("row_ror:8", R, g);
+  }
+  if (NV % 16 != 0) {
+    float* R = v + (NV - 8);
+    if (which == 0) SR_DPP8("quad_perm:[1,0,3,2]", R, g);
+    else if (which == 1) SR_DPP8("quad_perm:[2,3,0,1]", R, g);
+    else if (which == 2) SR_DPP8("row_half_mirror", R, g);
+    else SR_DPP8("row_ror:8", R, g);
   }
 }
 
