@@ -1,18 +1,22 @@
 // Fused rotate + sign flip + per-token asymmetric INT4 for gfx950: the fast
 // kernels for n = 28 * 2^9 (14336, the LLaMA3-8B down-projection input; seven
-// waves per token row) and n = 2^12, 2^13 (eight waves per row).
+// waves per token row), n = 56 * 2^9 (28672, the LLaMA3-70B one; fourteen
+// waves) and n = 2^12, 2^13 (eight waves).
 //
 // Index split.  A row x[i], i = a * 2^KB + b (a < KA, b < 2^KB), is read as
 // quads: b = 4 q + bb (q < NQ = 2^(KB-2), bb < 4).  The transform
-// H = H_KA (x) H_{2^KB} (KA = 28: Paley's order-28 matrix; KA = 32: the
-// Sylvester matrix, so H is the Sylvester matrix of order n) -- explainer
+// H = H_KA (x) H_{2^KB} (KA = 28: Paley's order-28 matrix; KA = 56: H28 (x) H2,
+// so that H28 (x) H_1024 reads as H56 (x) H_512 with a = 2 a28 + (top bit of
+// b); KA = 32: the Sylvester matrix, so H is the Sylvester matrix of order n)
+// -- explainer
 // "SignRot for 4-bit LLM quantization", paragraphs on rotation and on the
 // down-projection: a Hadamard matrix applied as a fast Walsh-Hadamard
 // transform -- is evaluated as
 //   stage 1 (MFMA): the KA-point mix over a together with the 4-point
 //     transform over bb, as v_mfma_f32_16x16x32_bf16 on the raw bf16 input.
-//     Rows m = (a' & 3, c) with c the output bb; k = (a, bb) in 4 chunks of
-//     eight a-rows; columns = 16 quads.  The weights are +-1, so every product
+//     Rows m = (a' & 3, c) with c the output bb; k = (a, bb) in KA / 8
+//     chunks of eight a-rows (the fourth of four half empty for KA = 28);
+//     columns = 16 quads.  The weights are +-1, so every product
 //     is exact and only the fp32 sums round.  Wave w owns a' = 4 w .. 4 w + 3,
 //     which splits the output rows over KA / 4 waves with no padding.
 //   stage 2 (VALU): the NQ-point transform over q: butterfly stages across
@@ -50,9 +54,10 @@ using namespace wave;
 
 template <int KA, int KB>
 struct FastShape {
-  static_assert(KA == 28 || KA == 32, "order-28 or Sylvester outer factor");
+  static_assert(KA == 28 || KA == 32 || KA == 56, "order-28, order-56 or Sylvester outer factor");
   static_assert(KB >= 7 && KB <= 9, "2 to 8 register tiles");
   static constexpr int kWaves = KA / 4;
+  static constexpr int NKC = (KA + 7) / 8;       // K chunks of eight a-rows
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int NQ = 1 << (KB - 2);       // quads per a-row
   static constexpr int NT = NQ / 16;             // register tiles
@@ -84,6 +89,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   using S = FastShape<KA, KB>;
   constexpr int NT = S::NT;
   constexpr int NV = S::NV;
+  constexpr bool kLateStage = (KA == 56);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -100,13 +106,13 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 
   // MFMA weights, A operand: lane (g, nl) holds A[m = nl][k = 8 g + i] with
   // m -> (a' = 4 w + (nl >> 2), c = nl & 3), k -> (a = 8 kc + 2 g + (i >> 2), bb = i & 3).
-  bf16x8_t wA[4];
+  bf16x8_t wA[S::NKC];
   {
     const int ap = 4 * w + (nl >> 2);
     const int cc = nl & 3;
     const int hrow = hka_sign<KA>(h28, ca, ap) * sig;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
+    for (int kc = 0; kc < S::NKC; ++kc)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ar = 8 * kc + 2 * g + (i >> 2);
@@ -244,6 +250,16 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     const int par = it & 1;
     const uint32_t bo = par ? static_cast<uint32_t>(S::kRowBytes) : 0u;
 
+    // (0) KA = 56 stages the next row here, before the MFMA stage, so that
+    // its registers are not live while the operands and the 28 weight
+    // registers are (the other shapes do it in (2), a longer lead time).
+    if (kLateStage && nxt < tokens) {
+      if (it == 0) wait_vmcnt<0>();
+      else if (YOUT) wait_vmcnt<1 + NT>();
+      else wait_vmcnt<1>();
+      write_row(bo ^ static_cast<uint32_t>(S::kRowBytes), par ^ 1);
+    }
+
     // (1) MFMA stage from this row's buffer
     float v[NV];
     {
@@ -251,20 +267,32 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const uint8_t* tp = lds + (base ^ (S::KMUL * t));
-        u32x4_t b[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) b[kc] = *reinterpret_cast<const u32x4_t*>(tp + 4 * S::PB * kc);
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // operands in groups of four chunks, or two for the seven chunks of
+        // KA = 56 (whose 28 weight registers leave less room)
+        constexpr int kGroup = S::NKC > 4 ? 2 : 4;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[kc], __builtin_bit_cast(bf16x8_t, b[kc]), acc, 0, 0, 0);
+        for (int k0 = 0; k0 < S::NKC; k0 += kGroup) {
+          u32x4_t b[kGroup];
+#pragma unroll
+          for (int kc = 0; kc < kGroup; ++kc)
+            if (k0 + kc < S::NKC) b[kc] = *reinterpret_cast<const u32x4_t*>(tp + 4 * S::PB * (k0 + kc));
+#pragma unroll
+          for (int kc = 0; kc < kGroup; ++kc)
+            if (k0 + kc < S::NKC)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[k0 + kc], __builtin_bit_cast(bf16x8_t, b[kc]), acc, 0,
+                                                            0, 0);
+          if (S::NKC > 4) __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[4 * t + r] = acc[r];
       }
     }
 
     // (2) stage the next row into the other buffer; start loading the one after
-    if (nxt < tokens) {
+    if (kLateStage) {
+      if (nn < tokens) load_row(nn);
+    } else if (nxt < tokens) {
       // The loads were issued a row ago; after them every wave issued the
       // previous row's code store (plus NT y stores with y_out); wave 0 also
       // scale and zero, so the same count only makes it wait longer.
@@ -301,28 +329,25 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     mn = fmin_raw(mn, v[NV - 1]);
     mx = fmax_raw(mx, v[NV - 1]);
     wave_minmax(mn, mx);
-    float* rd = red + 16 * par;
+    float* rd = red + 32 * par;  // per-wave min at rd[w], max at rd[16 + w]
     if (lane == 0) {
       rd[w] = mn;
-      rd[8 + w] = mx;
+      rd[16 + w] = mx;
     }
     lds_barrier();
-    {
-      const f32x4_t m0 = *reinterpret_cast<const f32x4_t*>(rd);
-      const f32x4_t m1 = *reinterpret_cast<const f32x4_t*>(rd + 4);
-      const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(rd + 8);
-      const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(rd + 12);
-      mn = m0[0];
-      min3_acc(mn, m0[1], m0[2]);
-      min3_acc(mn, m0[3], m1[0]);
-      min3_acc(mn, m1[1], m1[2]);
-      mx = x0[0];
-      max3_acc(mx, x0[1], x0[2]);
-      max3_acc(mx, x0[3], x1[0]);
-      max3_acc(mx, x1[1], x1[2]);
-      if constexpr (S::kWaves == 8) {
-        mn = fmin_raw(mn, m1[3]);
-        mx = fmax_raw(mx, x1[3]);
+#pragma unroll
+    for (int q = 0; q < S::kWaves; q += 4) {
+      const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(rd + q);
+      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(rd + 16 + q);
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+        if (q + k + 1 < S::kWaves) {
+          min3_acc(mn, m4[k], m4[k + 1]);
+          max3_acc(mx, x4[k], x4[k + 1]);
+        } else if (q + k < S::kWaves) {
+          mn = fmin_raw(mn, m4[k]);
+          mx = fmax_raw(mx, x4[k]);
+        }
       }
     }
 
@@ -373,12 +398,12 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 }
 
 template <int KA, int KB, bool YOUT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void rq_fast_kernel(RqArgs a) {
   using S = FastShape<KA, KB>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[S::kLdsBytes];
   __shared__ uint32_t dbits[S::N / 32];
-  __shared__ __attribute__((aligned(16))) float red[32];
+  __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float xcl[2];
   __shared__ int scratch[4];
   __shared__ uint32_t h28_lds[28];
@@ -426,17 +451,18 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool rq_fast_supports(int n, int k, bool m28) {
-  return (m28 && k == 9 && n == 14336) || (!m28 && (n == 4096 || n == 8192));
+  return (m28 && k == 9 && n == 14336) || (m28 && k == 10 && n == 28672) || (!m28 && (n == 4096 || n == 8192));
 }
 
 hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s) {
-  if (a.m28) return launch_shape<28, 9>(a, s);
+  if (a.m28) return a.n == 28672 ? launch_shape<56, 9>(a, s) : launch_shape<28, 9>(a, s);
   if (a.n == 4096) return launch_shape<32, 7>(a, s);
   return launch_shape<32, 8>(a, s);
 }
 
 const char* rq_fast_name(int n) {
   if (n == 14336) return "rq_mfma28_w7";
+  if (n == 28672) return "rq_mfma56_w14";
   if (n == 4096) return "rq_mfma32_w8_n4096";
   return "rq_mfma32_w8_n8192";
 }

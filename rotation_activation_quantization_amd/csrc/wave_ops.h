@@ -33,9 +33,13 @@ __device__ __forceinline__ uint16_t bf16_of_sign(int s) {
   return s > 0 ? 0x3f80u : (s < 0 ? 0xbf80u : 0u);
 }
 
+// Entry (row, col) of the outer Hadamard factor: Paley's H28 (row masks in
+// h28, bit set = -1), H56 = H28 (x) H2 (index 2 a + bit), or the Sylvester
+// matrix.
 template <int KA>
 __device__ __forceinline__ int hka_sign(const uint32_t* h28, int row, int col) {
   if (KA == 28) return ((h28[row] >> col) & 1u) ? -1 : 1;
+  if (KA == 56) return (((h28[row >> 1] >> (col >> 1)) ^ (row & col)) & 1u) ? -1 : 1;
   return (__popc(static_cast<uint32_t>(row & col)) & 1) ? -1 : 1;
 }
 
