@@ -463,8 +463,7 @@ hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s) {
 const char* rq_fast_name(int n) {
   if (n == 14336) return "rq_mfma28_w7";
   if (n == 28672) return "rq_mfma56_w14";
-  if (n == 4096) return "rq_mfma32_w8_n4096";
-  return "rq_mfma32_w8_n8192";
+  return "rq_mfma32_w8";
 }
 
 }  // namespace signrot

@@ -190,7 +190,7 @@ def test_no_outlier_control_batch():
 # --------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("n", [4096, 14336, 28, 2])
+@pytest.mark.parametrize("n", [4096, 8192, 14336, 28672, 28, 2])
 def test_degenerate_rows(n):
     c = n // 3
     rows = np.zeros((6, n), np.uint16)
@@ -207,12 +207,25 @@ def test_degenerate_rows(n):
     assert st["code_mismatches"] == 0
 
 
-def test_strided_rows_and_ragged_token_counts():
-    n = 14336
-    for t in (1, 3, 255, 257, 1031):
+@pytest.mark.parametrize("n,counts", [(14336, (1, 3, 255, 257, 1031)), (4096, (1, 5, 511, 513, 1537)),
+                                      (8192, (1, 7, 511, 513, 1031)), (28672, (1, 3, 255, 257, 521))])
+def test_strided_rows_and_ragged_token_counts(n, counts):
+    """Row stride ld = n + 64 and token counts around the launch grid (one
+    or several rows per workgroup, fewer rows than workgroups); rows are
+    compared with the oracle on a seeded sample that always holds the first
+    and last rows."""
+    for t in counts:
         bits = W.random_rows(t, n, seed=t, scale=0.7, outlier=1200.0)
         d = O.calibrate(bits)["d"]
-        check_rows(bits, d, f"ragged T={t}", ld=n + 64)
+        say(f"[gpu] ragged n={n} T={t} kernel={R.kernel_name(n)}")
+        codes, scale, zero, y = run(bits, d, y_out=True, ld=n + 64)
+        g = np.random.default_rng([11, n, t])
+        rows = np.unique(np.concatenate([[0, t - 1], g.choice(t, min(t, 24), replace=False)]))
+        st = compare(expected(bits[rows], d), codes[rows], scale[rows], zero[rows], y[rows], label=f"ragged n={n} T={t}")
+        say(f"[gpu] ragged n={n} T={t} rows={len(rows)}: {st}")
+        # every row: the extremes map to codes 0 and 15
+        q = O.unpack_int4(codes)
+        assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == 15)
 
 
 def test_zero_tokens_is_noop():
