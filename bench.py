@@ -109,6 +109,54 @@ def cpu_baseline(bits: np.ndarray, d: np.ndarray, budget_s: float = 12.0) -> dic
                       f"oracle rotate (float64 blocked dense product) + asymmetric INT4, {dt:.1f} s"}
 
 
+def bench_fold(args, torch, R, W) -> int:
+    """The offline weight fold on the LLaMA3-8B down-projection shape: W is
+    [4096 output features, 14336] bf16 (synthetic N(0, 1/n)), d from the same
+    calibration as the activations.  One step = one fold of the whole W."""
+    rows, n = 4096, 14336
+    g = torch.Generator(device="cpu").manual_seed(2611)
+    w = (torch.randn((rows, n), generator=g) / n ** 0.5).to(torch.bfloat16).cuda()
+    d = R.calibrate(to_dev_bits(W.calibration_batch("target")[0], torch))[0]
+    out = torch.empty((rows, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fn = R.lib().signrot_fold_weights
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step():
+        st = fn(w.data_ptr(), rows, n, n, d.data_ptr(), out.data_ptr(), sptr)
+        if st != 0:
+            R.check(st, "signrot_fold_weights")
+
+    for _ in range(args.warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    bpr = 2 * n + 4 * n  # bf16 row in, fp32 row out
+    achieved = bpr * rows / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "weight rows/s and achieved HBM GB/s, SignRot offline weight fold W' = W.H.D/sqrt(n)",
+        "value": rows * args.steps / wall, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"W {rows} x {n} bf16 N(0,1/n) (LLaMA3-8B down_proj shape) -> W' fp32",
+                   "kernel": R.kernel_name(n),
+                   "note": "the rotation kernels also write INT4 codes to a stream-ordered scratch "
+                           f"({n // 2 + 8} B/row, not counted)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_row": bpr,
+                     "kernel_avg_ms": ms},
+    }), flush=True)
+    return 0
+
+
 def workload_text(w, n: int, t: int, c: int) -> str:
     width = {4096: "2^12", 8192: "2^13", 14336: "28*2^9, LLaMA3-8B down_proj input",
              28672: "28*2^10, LLaMA3-70B down_proj input"}.get(n, str(n))
@@ -190,6 +238,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--fold", action="store_true",
+                    help="time the offline weight fold W' = W.H.D/sqrt(n) instead (W: 4096 x 14336 bf16)")
     ap.add_argument("--workload", default=WORKLOAD, choices=["cfg1", "cfg2", "cfg3", "target", "cfg4"],
                     help="synthetic workload to time (default: n=14336 x 8192 tokens)")
     args = ap.parse_args()
@@ -208,6 +258,8 @@ def main() -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.fold:
+        return bench_fold(args, torch, R, W)
     L = R.lib()
 
     wname = args.workload

@@ -125,6 +125,28 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
 int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero,
                     int64_t tokens, int64_t n, float* y_hat, void* stream);
 
+/*
+ * Offline weight fold (explainer, paragraph on the sign adjustment: the same
+ * flip is folded into the weights offline; paragraph on rotation: H / sqrt(n)
+ * is orthogonal, so rotating both factors of a product leaves it unchanged).
+ * For a down-projection out = x . W^T with W [rows][n] (one row per output
+ * feature), W' = W . H . D / sqrt(n): every row w of W becomes
+ * (w . H / sqrt(n)) (.) d, the very transform applied to the activations, so
+ * that out = x' . W'^T with x' = (x . H / sqrt(n)) (.) d.
+ *
+ *   w_bf16  device, [rows][ld] bf16, 16-byte aligned, ld >= n, ld % 8 == 0.
+ *   d       device, [n] int8, 16-byte aligned, entries +1/-1 (the vector
+ *           signrot_calibrate produced for the activations).
+ *   w_out   device, [rows][n] float, 16-byte aligned.
+ *
+ * Runs the rotation kernels of signrot_rotate_quant_int4, whose INT4 codes
+ * go to a stream-ordered scratch of rows * (n/2 + 8) bytes (hipMallocAsync /
+ * hipFreeAsync on `stream`) and are discarded.  Asynchronous.  rows == 0 is a
+ * no-op; argument errors as for signrot_rotate_quant_int4.
+ */
+int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,
+                         void* stream);
+
 /* Static text for a status code. */
 const char* signrot_strerror(int status);
 

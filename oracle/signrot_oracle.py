@@ -221,6 +221,16 @@ def rotate(x: np.ndarray, d: np.ndarray | None = None, block: int = 1024) -> np.
     return y
 
 
+def fold_weights(w_bits: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """Offline weight fold (explainer, paragraph on the sign adjustment: the
+    matching flip goes into the weights offline).  For out = x . W^T with W
+    [rows, n] bf16 bits, W' = W . H . D / sqrt(n): each row w becomes
+    (w . H / sqrt(n)) (.) d, so that x . W^T = x' . W'^T with
+    x' = (x . H / sqrt(n)) (.) d, because H D / sqrt(n) is orthogonal.
+    float64 [rows, n]."""
+    return rotate(bf16_bits_to_f64(w_bits), d)
+
+
 def fwht_textbook(x: np.ndarray) -> np.ndarray:
     """Unnormalised Walsh-Hadamard transform of each row by the iterative
     radix-2 butterfly recursion (natural order).  Used only to cross-check the

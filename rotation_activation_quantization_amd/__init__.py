@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_rotate_quant_int4.restype = ctypes.c_int
     L.signrot_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
     L.signrot_dequant.restype = ctypes.c_int
+    L.signrot_fold_weights.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    L.signrot_fold_weights.restype = ctypes.c_int
     L.signrot_strerror.argtypes = [ctypes.c_int]
     L.signrot_strerror.restype = ctypes.c_char_p
     L.signrot_last_error.argtypes = []
@@ -66,6 +68,7 @@ EXPORTED = (
     "signrot_calibrate",
     "signrot_rotate_quant_int4",
     "signrot_dequant",
+    "signrot_fold_weights",
     "signrot_strerror",
     "signrot_last_error",
     "signrot_debug_h28",
@@ -162,7 +165,22 @@ def signrot_dequant(codes, scale, zero, n: int | None = None):
     return y
 
 
+def signrot_fold_weights(w, d):
+    """Weights bf16 [rows, n] (one row per output feature of x . W^T) and the
+    activations' sign vector d -> W' = W . H . D / sqrt(n), float32 [rows, n]."""
+    import torch
+
+    ptr, rows, n, ld = _rows(w)
+    if d.dtype != torch.int8 or d.numel() != n or not d.is_contiguous():
+        raise ValueError("d must be a contiguous int8 tensor of n entries")
+    out = torch.empty((rows, n), dtype=torch.float32, device=w.device)
+    check(lib().signrot_fold_weights(ptr, rows, n, ld, d.data_ptr(), out.data_ptr(), _stream_of(w)),
+          "signrot_fold_weights")
+    return out
+
+
 # short aliases
 calibrate = signrot_calibrate
 rotate_quant_int4 = signrot_rotate_quant_int4
 dequant = signrot_dequant
+fold_weights = signrot_fold_weights

@@ -183,6 +183,51 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   return SIGNROT_OK;
 }
 
+int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,
+                         void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  if (!sh.ok) {
+    set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (rows < 0) return fail_einval("rows < 0");
+  if (ld < n) return fail_einval("ld < n");
+  if (ld & 7) return fail_einval("ld must be a multiple of 8");
+  if (rows == 0) return SIGNROT_OK;
+  if (rows > (int64_t{1} << 40)) return fail_einval("rows too large");
+  if (!w_bf16 || !d || !w_out) return fail_einval("null device pointer");
+  if (!aligned16(w_bf16) || !aligned16(d) || !aligned16(w_out)) return fail_einval("w, d and w_out must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // scratch: codes [rows][n/2], then (16-byte aligned) scale [rows] and zero [rows]
+  const size_t code_bytes = (static_cast<size_t>(rows) * static_cast<size_t>(n / 2) + 15) & ~size_t{15};
+  uint8_t* scratch = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), code_bytes + 8 * static_cast<size_t>(rows), s);
+  if (e != hipSuccess) return fail_hip(e, "hipMallocAsync");
+  float* scale = reinterpret_cast<float*>(scratch + code_bytes);
+  RqArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = static_cast<const uint16_t*>(w_bf16);
+  a.d = d;
+  a.codes = scratch;
+  a.scale = scale;
+  a.zero = scale + rows;
+  a.yout = w_out;
+  a.tokens = rows;
+  a.ld = ld;
+  a.n = sh.n;
+  a.k = sh.k;
+  a.m28 = sh.m28 ? 1 : 0;
+  a.inv_sqrt_n = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
+  a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
+  for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, s) : launch_rq_generic(a, s);
+  const hipError_t ef = hipFreeAsync(scratch, s);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return fail_hip(e, "fold_weights launch");
+  return SIGNROT_OK;
+}
+
 int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens, int64_t n,
                     float* y_hat, void* stream) {
   g_last_error[0] = '\0';

@@ -118,3 +118,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(R, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         R.lib()
+
+
+def test_fold_weights_argument_errors(L):
+    def fold(w=FAKE, rows=4, n=4096, ld=4096, d=FAKE, out=FAKE):
+        return L.signrot_fold_weights(w, rows, n, ld, d, out, None)
+
+    assert fold(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert fold(rows=-1) == R.SIGNROT_EINVAL
+    assert fold(ld=4095) == R.SIGNROT_EINVAL
+    assert fold(w=None) == R.SIGNROT_EINVAL
+    assert fold(d=None) == R.SIGNROT_EINVAL
+    assert fold(out=None) == R.SIGNROT_EINVAL
+    assert fold(out=FAKE + 4) == R.SIGNROT_EINVAL
+    assert fold(rows=0, w=None, d=None, out=None) == R.SIGNROT_OK

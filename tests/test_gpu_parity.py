@@ -8,6 +8,7 @@ seeded sample of rows one by one; properties that hold at any size are
 checked on every row.
 """
 
+import math
 import os
 import sys
 
@@ -275,3 +276,58 @@ def test_gpu_round_trip_mse_matches_oracle():
     m_ps = O.mse(yp, O.dequant_sym(qs, ss))
     assert np.all(m_gpu[out] * 10 < m_ps[out])
     say(f"[gpu] MSE outlier tokens gpu={m_gpu[out].mean():.5f} plain_sym={m_ps[out].mean():.5f}")
+
+
+@pytest.mark.parametrize("n", [4096, 14336, 28672, 1792])
+def test_fold_weights_matches_oracle(n):
+    """W' = W . H . D / sqrt(n) on the GPU (the rotation kernels with their
+    codes discarded) against the oracle, within the rotated-value tolerance."""
+    g = np.random.default_rng([41, n])
+    rows = 48
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((rows, n)) / np.sqrt(n)).astype(np.float32))
+    x_cal = W.random_rows(16, n, seed=5, scale=0.7, outlier=1300.0)
+    d_np = O.calibrate(x_cal)["d"]
+    say(f"[gpu] fold n={n} rows={rows} kernel={R.kernel_name(n)}")
+    wf = R.fold_weights(to_dev(w_bits), torch.from_numpy(d_np).cuda())
+    torch.cuda.synchronize()
+    ref = O.fold_weights(w_bits, d_np)
+    err = np.abs(wf.cpu().numpy() - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    say(f"[gpu] fold n={n}: max rel err {err.max():.2e}")
+    assert err.max() <= 1e-5
+
+
+def test_fold_and_quantized_activations_reproduce_the_projection():
+    """End to end at n = 14336: dequant(codes of x) . W'^T approximates x . W^T
+    (float64) to within the INT4 quantization error, and on outlier tokens
+    SignRot + asymmetric INT4 is far closer than plain Hadamard + symmetric."""
+    n, rows = 14336, 64
+    bits, meta = W.batch("cfg3", tokens=32)
+    d_np = O.calibrate(W.calibration_batch("cfg3")[0])["d"]
+    g = np.random.default_rng([43])
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((rows, n)) / np.sqrt(n)).astype(np.float32))
+    d = torch.from_numpy(d_np).cuda()
+    say("[gpu] fold end-to-end n=14336")
+    wf = R.fold_weights(to_dev(w_bits), d)
+    codes, scale, zero = R.rotate_quant_int4(to_dev(bits), d)
+    out_q = (R.dequant(codes, scale, zero).double() @ wf.double().T).cpu().numpy()
+    torch.cuda.synchronize()
+    x = O.bf16_bits_to_f64(bits)
+    wt = O.bf16_bits_to_f64(w_bits)
+    ref = x @ wt.T
+    # plain Hadamard + symmetric INT4 on the same tokens, folded weights without the flip
+    yp = O.rotate(x)
+    qs, ss = O.quant_sym(yp)
+    out_sym = O.dequant_sym(qs, ss) @ O.rotate(wt).T
+    # each output sums n rounding errors, uniform within +-s/2 of the token's
+    # step s, weighted by a row of W': a 6-sigma bound per output
+    wn = np.linalg.norm(wf.cpu().numpy().astype(np.float64), axis=1)
+    sc = scale.cpu().numpy().astype(np.float64)
+    bound = 6.0 * sc[:, None] / math.sqrt(12.0) * wn[None, :] + 1e-6 * np.abs(ref)
+    assert np.all(np.abs(out_q - ref) <= bound)
+    rms_q = np.sqrt(((out_q - ref) ** 2).mean(axis=1))
+    rms_s = np.sqrt(((out_sym - ref) ** 2).mean(axis=1))
+    out = meta["outlier_tokens"][meta["outlier_tokens"] < 32]
+    assert len(out) > 0
+    assert np.all(rms_q[out] * 3 < rms_s[out])
+    say(f"[gpu] fold end-to-end: rms err signrot/asym {rms_q[out].mean():.3e}, plain/sym {rms_s[out].mean():.3e} "
+        f"on {len(out)} outlier tokens")

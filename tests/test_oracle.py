@@ -486,3 +486,33 @@ def test_mse_grid_is_the_oracles():
     assert g["outlier"]["tokens"] == int(has.sum())
     assert abs(m[has].mean() - g["outlier"]["signrot_asym"]) <= 1e-12 * g["outlier"]["signrot_asym"]
     assert abs(m[~has].mean() - g["no_outlier"]["signrot_asym"]) <= 1e-12 * g["no_outlier"]["signrot_asym"]
+
+
+@pytest.mark.parametrize("n", [28, 56, 64, 112, 256])
+def test_fold_preserves_the_down_projection(n):
+    """x . W^T = x' . W'^T exactly (float64 round-off) for the rotated and
+    flipped activations x' and the folded weights W', with the calibrated
+    sign vector: the fold undoes the activation transform inside the product."""
+    g = np.random.default_rng([31, n])
+    x_bits = W.f32_to_bf16_bits(g.standard_normal((5, n)).astype(np.float32))
+    x_bits[:, n // 3] = W.f32_to_bf16_bits(np.full(5, 900.0, np.float32))
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((7, n)) / np.sqrt(n)).astype(np.float32))
+    d = O.calibrate(x_bits)["d"]
+    x = O.bf16_bits_to_f64(x_bits)
+    wt = O.bf16_bits_to_f64(w_bits)
+    ref = x @ wt.T
+    got = O.rotate(x, d) @ O.fold_weights(w_bits, d).T
+    assert np.allclose(got, ref, rtol=0, atol=1e-12 * np.abs(x).max() * np.abs(wt).max() * n)
+
+
+@pytest.mark.parametrize("n", [28, 64, 14336])
+def test_fold_of_unit_rows_is_the_flipped_hadamard_row(n):
+    """Folding the unit row e_j gives d (.) H[j, :] / sqrt(n): row j of H, built
+    entry by entry from the Kronecker definition."""
+    j = (5 * n) // 7
+    w = np.zeros((1, n), np.uint16)
+    w[0, j] = 0x3F80  # bf16 1.0
+    d = np.where(np.arange(n) % 3 == 0, -1, 1).astype(np.int8)
+    got = O.fold_weights(w, d)[0]
+    want = d.astype(np.float64) * O.hadamard_row(n, j).astype(np.float64) / math.sqrt(n)
+    assert np.array_equal(got, want)
