@@ -157,6 +157,115 @@ def bench_fold(args, torch, R, W) -> int:
     return 0
 
 
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def bench_linear(args, torch, R, W) -> int:
+    """The consumer product on the LLaMA3-8B down-projection shape: 8192 tokens
+    of INT4 activations (codes, scale, zero from signrot_rotate_quant_int4 on
+    the n = 14336 workload) times the folded weight W' [4096, 14336] bf16
+    (synthetic N(0, 1/n), folded with the same d).  One step = one
+    signrot_int4_linear call over the whole batch."""
+    rows = 4096
+    bits, _ = W.batch("target")
+    t, n = bits.shape
+    d = R.calibrate(to_dev_bits(W.calibration_batch("target")[0], torch))[0]
+    codes, scale, zero = R.rotate_quant_int4(to_dev_bits(bits, torch), d)
+    g = torch.Generator(device="cpu").manual_seed(2612)
+    w = (torch.randn((rows, n), generator=g) / n ** 0.5).to(torch.bfloat16).cuda()
+    wf = R.fold_weights(w, d).to(torch.bfloat16)
+    del w
+    rs = R.weight_rowsum(wf)
+    out = torch.empty((t, rows), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    fn = R.lib().signrot_int4_linear
+    argv = (codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), t, n, wf.data_ptr(), n, rs.data_ptr(), rows,
+            out.data_ptr(), sptr)
+
+    def step():
+        st = fn(*argv)
+        if st != 0:
+            R.check(st, "signrot_int4_linear")
+
+    def timed(body, steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(steps):
+            body()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / steps
+
+    for _ in range(args.warmup):
+        step()
+    wall, ms = timed(step, args.steps)
+    flops = 2.0 * t * n * rows
+    achieved = flops / (ms * 1e-3) / 1e12
+    # context: the library bf16 GEMM (hipBLASLt via torch) on the same shape,
+    # with the activations already dequantized to bf16
+    yb = R.dequant(codes, scale, zero).to(torch.bfloat16)
+    wt = wf.t()
+    for _ in range(20):
+        torch.matmul(yb, wt)
+    _, ms_lib = timed(lambda: torch.matmul(yb, wt), 50)
+    del yb
+    line = {
+        "metric": "tokens/s and achieved TFLOP/s, INT4-activation down-projection with zero-point correction",
+        "value": t * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x u4 -> f32", "data": "synthetic",
+        "config": {"workload": f"{t} tokens x n={n} INT4 codes (n=14336 workload, quantized on the GPU) "
+                               f"times W' [{rows} x {n}] bf16, out f32 [{t} x {rows}]",
+                   "kernel": R.int4_linear_kernel_name(codes, wf),
+                   "library_bf16_gemm_ms": ms_lib,
+                   "library_bf16_gemm_tflops": flops / (ms_lib * 1e-3) / 1e12},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "flops_per_launch": flops,
+                     "kernel_avg_ms": ms},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_linear(codes, scale, zero, wf)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_linear(codes, scale, zero, wf, budget_s: float = 12.0) -> dict:
+    """The oracle's int4_linear (float64 dequantize, then numpy matmul) on
+    32-token chunks of the same operands, for about budget_s seconds."""
+    import oracle as O
+
+    c = codes.cpu().numpy()
+    s = scale.cpu().numpy()
+    z = zero.cpu().numpy()
+    wb = wf.view(torch_int16()).cpu().numpy().view(np.uint16)
+    chunk, done = 32, 0
+    t0 = time.perf_counter()
+    while done + chunk <= c.shape[0]:
+        O.int4_linear(c[done:done + chunk], s[done:done + chunk], z[done:done + chunk], wb)
+        done += chunk
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} tokens x {wb.shape[0]} rows of the same operands, oracle int4_linear "
+                      f"(float64 dequantize + matmul), {dt:.1f} s"}
+
+
+def torch_int16():
+    import torch
+
+    return torch.int16
+
+
 def workload_text(w, n: int, t: int, c: int) -> str:
     width = {4096: "2^12", 8192: "2^13", 14336: "28*2^9, LLaMA3-8B down_proj input",
              28672: "28*2^10, LLaMA3-70B down_proj input"}.get(n, str(n))
@@ -240,6 +349,9 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--fold", action="store_true",
                     help="time the offline weight fold W' = W.H.D/sqrt(n) instead (W: 4096 x 14336 bf16)")
+    ap.add_argument("--linear", action="store_true",
+                    help="time the INT4-activation down-projection signrot_int4_linear instead "
+                         "(8192 x 14336 codes, W' 4096 x 14336 bf16)")
     ap.add_argument("--workload", default=WORKLOAD, choices=["cfg1", "cfg2", "cfg3", "target", "cfg4"],
                     help="synthetic workload to time (default: n=14336 x 8192 tokens)")
     args = ap.parse_args()
@@ -260,6 +372,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.fold:
         return bench_fold(args, torch, R, W)
+    if args.linear:
+        return bench_linear(args, torch, R, W)
     L = R.lib()
 
     wname = args.workload

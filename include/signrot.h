@@ -147,6 +147,56 @@ int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero,
 int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,
                          void* stream);
 
+/*
+ * Row sums of a folded weight, rowsum[k] = sum_j w[k][j] (explainer,
+ * paragraph on symmetric versus asymmetric quantizers: the zero-point's share
+ * of the product is the zero-point times a precomputed sum of the weights).
+ * Computed once per weight, offline.
+ *
+ *   w_bf16  device, [rows][ld] bf16 (W' = W . H . D / sqrt(n) rounded to
+ *           bf16), ld >= n; no alignment requirement.
+ *   rowsum  device, [rows] float: the exact sum of the bf16 values,
+ *           accumulated in binary64 and rounded once.
+ *
+ * rows == 0 is a no-op; rows < 0, n < 0, ld < n or a null pointer ->
+ * SIGNROT_EINVAL.  Any n (the sum does not depend on the Hadamard order).
+ * Asynchronous.
+ */
+int signrot_weight_rowsum(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, float* rowsum, void* stream);
+
+/*
+ * The consumer of the INT4 activations: the down-projection on the folded
+ * weight, out = yhat . W'^T with yhat = scale * (q - zero), evaluated as
+ * (explainer, paragraph on symmetric versus asymmetric quantizers)
+ *
+ *   out[t][k] = scale[t] * (sum_j q[t][j] * w[k][j] - zero[t] * rowsum[k]),
+ *
+ * so the product itself runs on the unsigned integer codes.
+ *
+ *   codes   device, [tokens][n/2] uint8, as signrot_rotate_quant_int4 writes
+ *           them (channel 2m in the low nibble of byte m).
+ *   scale   device, [tokens] float; zero device, [tokens] float.
+ *   w_bf16  device, [rows][ldw] bf16: row k is output feature k of W'.
+ *   rowsum  device, [rows] float, from signrot_weight_rowsum.
+ *   out     device, [tokens][rows] float.
+ *
+ * n even and >= 2 (any Hadamard order), ldw >= n.  The MFMA kernel runs when
+ * n % 64 == 0, ldw % 8 == 0, rows * ldw < 2^31 and codes and w are 16-byte
+ * aligned; other shapes take a plain one-thread-per-output kernel.  The
+ * integer-by-bf16 products are exact; they are summed in binary32 (in an
+ * order that differs between the two kernels).  tokens == 0 or rows == 0 is a
+ * no-op; negative sizes, odd n, ldw < n, tokens or rows >= 2^31 or a null
+ * pointer -> SIGNROT_EINVAL.  Asynchronous.
+ */
+int signrot_int4_linear(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens, int64_t n,
+                        const void* w_bf16, int64_t ldw, const float* rowsum, int64_t rows, float* out,
+                        void* stream);
+
+/* Which kernel signrot_int4_linear would launch for these operands (a static
+ * string), or NULL when the arguments are invalid. */
+const char* signrot_int4_linear_kernel_name(const uint8_t* codes, int64_t tokens, int64_t n, const void* w_bf16,
+                                            int64_t ldw, int64_t rows);
+
 /* Static text for a status code. */
 const char* signrot_strerror(int status);
 

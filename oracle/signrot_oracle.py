@@ -344,6 +344,28 @@ def mse(y: np.ndarray, y_hat: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# The consumer product  ([expl] symmetric-vs-asymmetric paragraph: with an
+# asymmetric quantizer the matrix multiply also needs the zero-point times a
+# precomputed sum of the weights)
+# ---------------------------------------------------------------------------
+
+
+def weight_rowsum(w_bits: np.ndarray) -> np.ndarray:
+    """Sum of each row of a bf16 weight [rows, n] (one row per output
+    feature), float64."""
+    return bf16_bits_to_f64(w_bits).sum(axis=1)
+
+
+def int4_linear(codes: np.ndarray, scale: np.ndarray, zero: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """The down-projection on the quantized activations: dequantize every code
+    to its level, yhat = scale * (q - zero), then multiply by the folded
+    weight, out = yhat . W'^T.  codes packed [T, n/2], W' bf16 bits
+    [rows, n] -> float64 [T, rows]."""
+    yhat = dequant(unpack_int4(codes), scale, zero)
+    return yhat @ bf16_bits_to_f64(w_bits).T
+
+
+# ---------------------------------------------------------------------------
 # The whole online path, end to end
 # ---------------------------------------------------------------------------
 

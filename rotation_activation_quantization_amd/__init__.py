@@ -51,6 +51,12 @@ def lib() -> ctypes.CDLL:
     L.signrot_dequant.restype = ctypes.c_int
     L.signrot_fold_weights.argtypes = [vp, i64, i64, i64, vp, vp, vp]
     L.signrot_fold_weights.restype = ctypes.c_int
+    L.signrot_weight_rowsum.argtypes = [vp, i64, i64, i64, vp, vp]
+    L.signrot_weight_rowsum.restype = ctypes.c_int
+    L.signrot_int4_linear.argtypes = [vp, vp, vp, i64, i64, vp, i64, vp, i64, vp, vp]
+    L.signrot_int4_linear.restype = ctypes.c_int
+    L.signrot_int4_linear_kernel_name.argtypes = [vp, i64, i64, vp, i64, i64]
+    L.signrot_int4_linear_kernel_name.restype = ctypes.c_char_p
     L.signrot_strerror.argtypes = [ctypes.c_int]
     L.signrot_strerror.restype = ctypes.c_char_p
     L.signrot_last_error.argtypes = []
@@ -69,6 +75,9 @@ EXPORTED = (
     "signrot_rotate_quant_int4",
     "signrot_dequant",
     "signrot_fold_weights",
+    "signrot_weight_rowsum",
+    "signrot_int4_linear",
+    "signrot_int4_linear_kernel_name",
     "signrot_strerror",
     "signrot_last_error",
     "signrot_debug_h28",
@@ -179,8 +188,56 @@ def signrot_fold_weights(w, d):
     return out
 
 
+def signrot_weight_rowsum(w):
+    """bf16 [rows, n] -> rowsum f32 [rows], the exact sum of each row."""
+    import torch
+
+    ptr, rows, n, ld = _rows(w)
+    out = torch.empty(rows, dtype=torch.float32, device=w.device)
+    check(lib().signrot_weight_rowsum(ptr, rows, n, ld, out.data_ptr(), _stream_of(w)), "signrot_weight_rowsum")
+    return out
+
+
+def _linear_operands(codes, w):
+    import torch
+
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous 2-D uint8 tensor")
+    ptr, rows, n, ld = _rows(w)
+    if codes.shape[1] * 2 != n:
+        raise ValueError(f"codes hold {codes.shape[1] * 2} channels, w has {n}")
+    return ptr, rows, n, ld
+
+
+def signrot_int4_linear(codes, scale, zero, w, rowsum, out=None):
+    """INT4 activations (codes u8 [T, n/2], scale/zero f32 [T]) times the folded
+    weight w bf16 [rows, n] -> f32 [T, rows] = (scale * (q - zero)) . w^T,
+    with rowsum = signrot_weight_rowsum(w)."""
+    import torch
+
+    wptr, rows, n, ld = _linear_operands(codes, w)
+    t = codes.shape[0]
+    for name, v, size in (("scale", scale, t), ("zero", zero, t), ("rowsum", rowsum, rows)):
+        if v.dtype != torch.float32 or v.numel() != size or not v.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {size} entries")
+    if out is None:
+        out = torch.empty((t, rows), dtype=torch.float32, device=codes.device)
+    check(lib().signrot_int4_linear(codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), t, n, wptr, ld,
+                                    rowsum.data_ptr(), rows, out.data_ptr(), _stream_of(codes)),
+          "signrot_int4_linear")
+    return out
+
+
+def int4_linear_kernel_name(codes, w) -> str | None:
+    wptr, rows, n, ld = _linear_operands(codes, w)
+    r = lib().signrot_int4_linear_kernel_name(codes.data_ptr(), codes.shape[0], n, wptr, ld, rows)
+    return r.decode() if r else None
+
+
 # short aliases
 calibrate = signrot_calibrate
 rotate_quant_int4 = signrot_rotate_quant_int4
 dequant = signrot_dequant
 fold_weights = signrot_fold_weights
+weight_rowsum = signrot_weight_rowsum
+int4_linear = signrot_int4_linear

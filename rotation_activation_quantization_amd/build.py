@@ -20,6 +20,7 @@ SOURCES = [
     "rq_generic.hip",
     "rq_fast.hip",
     "calib_dequant.hip",
+    "linear.hip",
     "hadamard28.cpp",
 ]
 

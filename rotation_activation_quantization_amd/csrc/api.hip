@@ -245,4 +245,62 @@ int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero,
   return SIGNROT_OK;
 }
 
+int signrot_weight_rowsum(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, float* rowsum, void* stream) {
+  g_last_error[0] = '\0';
+  if (rows < 0 || n < 0) return fail_einval("rows and n must be >= 0");
+  if (ld < n) return fail_einval("ld < n");
+  if (rows == 0) return SIGNROT_OK;
+  if (rows > (int64_t{1} << 31) - 1) return fail_einval("rows too large");
+  if (!w_bf16 || !rowsum) return fail_einval("null device pointer");
+  hipError_t e = launch_weight_rowsum(static_cast<const uint16_t*>(w_bf16), rows, n, ld, rowsum,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "weight_rowsum launch");
+  return SIGNROT_OK;
+}
+
+namespace {
+int fill_linear(LinearArgs& a, const uint8_t* codes, const float* scale, const float* zero, int64_t tokens,
+                int64_t n, const void* w_bf16, int64_t ldw, const float* rowsum, int64_t rows, float* out) {
+  if (tokens < 0 || rows < 0) return fail_einval("tokens and rows must be >= 0");
+  if (n < 2 || (n & 1)) return fail_einval("n must be even and >= 2");
+  if (n > (int64_t{1} << 30)) return fail_einval("n too large");
+  if (ldw < n) return fail_einval("ldw < n");
+  if (tokens > (int64_t{1} << 31) - 1 || rows > (int64_t{1} << 31) - 1) return fail_einval("tokens or rows too large");
+  memset(&a, 0, sizeof(a));
+  a.codes = codes;
+  a.scale = scale;
+  a.zero = zero;
+  a.w = static_cast<const uint16_t*>(w_bf16);
+  a.rowsum = rowsum;
+  a.out = out;
+  a.ldw = ldw;
+  a.T = static_cast<int>(tokens);
+  a.R = static_cast<int>(rows);
+  a.n = static_cast<int>(n);
+  return SIGNROT_OK;
+}
+}  // namespace
+
+int signrot_int4_linear(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens, int64_t n,
+                        const void* w_bf16, int64_t ldw, const float* rowsum, int64_t rows, float* out,
+                        void* stream) {
+  g_last_error[0] = '\0';
+  LinearArgs a;
+  const int st = fill_linear(a, codes, scale, zero, tokens, n, w_bf16, ldw, rowsum, rows, out);
+  if (st != SIGNROT_OK) return st;
+  if (tokens == 0 || rows == 0) return SIGNROT_OK;
+  if (!codes || !scale || !zero || !w_bf16 || !rowsum || !out) return fail_einval("null device pointer");
+  hipError_t e = launch_int4_linear(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "int4_linear launch");
+  return SIGNROT_OK;
+}
+
+const char* signrot_int4_linear_kernel_name(const uint8_t* codes, int64_t tokens, int64_t n, const void* w_bf16,
+                                            int64_t ldw, int64_t rows) {
+  LinearArgs a;
+  if (fill_linear(a, codes, nullptr, nullptr, tokens, n, w_bf16, ldw, nullptr, rows, nullptr) != SIGNROT_OK)
+    return nullptr;
+  return int4_linear_name(a);
+}
+
 }  // extern "C"

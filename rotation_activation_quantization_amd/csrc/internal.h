@@ -62,4 +62,25 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float*
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// The consumer GEMM: out[t][k] = scale[t] * (sum_j q[t][j] w[k][j] - zero[t] * rowsum[k]).
+struct LinearArgs {
+  const uint8_t* codes;  // [T][n/2], packed as signrot_rotate_quant_int4 writes them
+  const float* scale;    // [T]
+  const float* zero;     // [T]
+  const uint16_t* w;     // bf16 bits, [R][ldw]
+  const float* rowsum;   // [R]
+  float* out;            // [T][R]
+  int64_t ldw;
+  int T;
+  int R;
+  int n;
+  int tiles_m;  // set by the launcher
+  int tiles_n;
+};
+bool int4_linear_fast_ok(const LinearArgs& a);
+const char* int4_linear_name(const LinearArgs& a);
+hipError_t launch_int4_linear(LinearArgs a, hipStream_t s);
+hipError_t launch_weight_rowsum(const uint16_t* w, int64_t rows, int64_t n, int64_t ld, float* rowsum,
+                                hipStream_t s);
+
 }  // namespace signrot

@@ -132,3 +132,46 @@ def test_fold_weights_argument_errors(L):
     assert fold(out=None) == R.SIGNROT_EINVAL
     assert fold(out=FAKE + 4) == R.SIGNROT_EINVAL
     assert fold(rows=0, w=None, d=None, out=None) == R.SIGNROT_OK
+
+
+def test_weight_rowsum_argument_errors(L):
+    def rs(w=FAKE, rows=4, n=4096, ld=4096, out=FAKE):
+        return L.signrot_weight_rowsum(w, rows, n, ld, out, None)
+
+    assert rs(rows=-1) == R.SIGNROT_EINVAL
+    assert rs(n=-2) == R.SIGNROT_EINVAL
+    assert rs(ld=4095) == R.SIGNROT_EINVAL
+    assert rs(w=None) == R.SIGNROT_EINVAL
+    assert rs(out=None) == R.SIGNROT_EINVAL
+    assert rs(rows=0, w=None, out=None) == R.SIGNROT_OK
+
+
+def test_int4_linear_argument_errors(L):
+    def lin(codes=FAKE, scale=FAKE, zero=FAKE, t=8, n=4096, w=FAKE, ldw=4096, rowsum=FAKE, rows=16, out=FAKE):
+        return L.signrot_int4_linear(codes, scale, zero, t, n, w, ldw, rowsum, rows, out, None)
+
+    assert lin(t=-1) == R.SIGNROT_EINVAL
+    assert lin(rows=-1) == R.SIGNROT_EINVAL
+    assert lin(n=4095) == R.SIGNROT_EINVAL
+    assert lin(n=0) == R.SIGNROT_EINVAL
+    assert lin(ldw=4094) == R.SIGNROT_EINVAL
+    assert lin(t=1 << 31) == R.SIGNROT_EINVAL
+    for k in ("codes", "scale", "zero", "w", "rowsum", "out"):
+        assert lin(**{k: None}) == R.SIGNROT_EINVAL, k
+    assert lin(t=0, codes=None, scale=None, zero=None, out=None) == R.SIGNROT_OK
+    assert lin(rows=0, w=None, rowsum=None, out=None) == R.SIGNROT_OK
+
+
+def test_int4_linear_kernel_choice(L):
+    def name(codes=FAKE, t=8, n=4096, w=FAKE, ldw=4096, rows=16):
+        r = L.signrot_int4_linear_kernel_name(codes, t, n, w, ldw, rows)
+        return r.decode() if r else None
+
+    assert name() == "int4_linear_mfma"
+    assert name(n=14336, ldw=14336) == "int4_linear_mfma"
+    assert name(n=28, ldw=32) == "int4_linear_simple"      # n % 64 != 0
+    assert name(ldw=4100) == "int4_linear_simple"           # rows not 16-byte aligned
+    assert name(w=FAKE + 2) == "int4_linear_simple"
+    assert name(codes=FAKE + 8) == "int4_linear_simple"
+    assert name(rows=1 << 20, n=4096, ldw=4096) == "int4_linear_simple"  # rows * ldw >= 2^31
+    assert name(n=7) is None

@@ -516,3 +516,96 @@ def test_fold_of_unit_rows_is_the_flipped_hadamard_row(n):
     got = O.fold_weights(w, d)[0]
     want = d.astype(np.float64) * O.hadamard_row(n, j).astype(np.float64) / math.sqrt(n)
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# The consumer product (explainer, paragraph on symmetric versus asymmetric
+# quantizers: the zero-point's share is the zero-point times a precomputed sum
+# of the weights)
+# ---------------------------------------------------------------------------
+
+
+def _nibble(codes, t, j):
+    b = int(codes[t, j // 2])
+    return (b >> 4) if (j & 1) else (b & 15)
+
+
+def test_int4_linear_brute_force_on_a_tiny_case():
+    """Dequantize-then-multiply equals the sum, written out term by term from
+    the nibbles, of scale * (q - zero) * w."""
+    g = np.random.default_rng(71)
+    t, n, rows = 3, 10, 4
+    codes = g.integers(0, 256, size=(t, n // 2), dtype=np.uint8)
+    scale = np.array([0.5, 0.03125, 2.0])
+    zero = np.array([-3.25, 7.0, 80.5])
+    w_bits = W.f32_to_bf16_bits(g.standard_normal((rows, n)).astype(np.float32))
+    wv = O.bf16_bits_to_f64(w_bits)
+    got = O.int4_linear(codes, scale, zero, w_bits)
+    for ti in range(t):
+        for k in range(rows):
+            want = 0.0
+            for j in range(n):
+                want += scale[ti] * (_nibble(codes, ti, j) - zero[ti]) * wv[k, j]
+            assert abs(got[ti, k] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_int4_linear_zero_point_form_is_exact_on_integers():
+    """With integer weights, a power-of-two scale and an integer zero-point
+    every quantity is an integer times the scale, so the integer-GEMM form
+    scale * (q . W^T - zero * rowsum(W)) -- evaluated here in int64 -- equals
+    the dequantize-then-multiply definition exactly."""
+    g = np.random.default_rng(72)
+    t, n, rows = 6, 96, 5
+    codes = g.integers(0, 256, size=(t, n // 2), dtype=np.uint8)
+    wi = g.integers(-8, 9, size=(rows, n))
+    w_bits = W.f32_to_bf16_bits(wi.astype(np.float32))
+    scale = np.ldexp(1.0, g.integers(-6, 3, size=t)).astype(np.float64)
+    zero = g.integers(-90, 20, size=t).astype(np.float64)
+    q = np.empty((t, n), np.int64)
+    for ti in range(t):
+        for j in range(n):
+            q[ti, j] = _nibble(codes, ti, j)
+    rowsum = wi.sum(axis=1)
+    want = scale[:, None] * (q @ wi.T - zero.astype(np.int64)[:, None] * rowsum[None, :])
+    assert np.array_equal(O.int4_linear(codes, scale, zero, w_bits), want)
+    assert np.array_equal(O.weight_rowsum(w_bits), rowsum.astype(np.float64))
+
+
+@pytest.mark.parametrize("n", [28, 512, 14336])
+def test_rowsum_of_the_folded_weight_is_one_weight_column(n):
+    """With d = sigma * (row c of H), W' . 1 = W . H . d / sqrt(n) =
+    sigma * sqrt(n) * W[:, c], because the rows of H are orthogonal with norm
+    sqrt(n): the whole sum of a folded weight row is the outlier channel's
+    weight."""
+    g = np.random.default_rng([73, n])
+    c = (3 * n) // 5
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((6, n)) / np.sqrt(n)).astype(np.float32))
+    for sigma in (1, -1):
+        d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+        folded = O.fold_weights(w_bits, d)
+        want = sigma * math.sqrt(n) * O.bf16_bits_to_f64(w_bits)[:, c]
+        assert np.allclose(folded.sum(axis=1), want, rtol=0, atol=1e-12 * math.sqrt(n))
+
+
+@pytest.mark.parametrize("n", [28, 1024])
+def test_quantized_product_on_the_folded_weight_approximates_the_projection(n):
+    """The whole chain -- calibrate, rotate + flip + INT4 on the activations,
+    fold + bf16 rounding on the weights, dequantized product -- stays within
+    its rigorous error bound of x . W^T:
+    |out - x W^T| <= (s/2) sum_j |W'_bf16| + sum_j |y_j| |W'_bf16 - W'|,
+    since x W^T = y W'^T exactly and every level is within s/2 of its value."""
+    g = np.random.default_rng([74, n])
+    x_bits = W.f32_to_bf16_bits(g.standard_normal((9, n)).astype(np.float32))
+    x_bits[:, n // 4] = W.f32_to_bf16_bits(np.full(9, 600.0, np.float32))
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((11, n)) / np.sqrt(n)).astype(np.float32))
+    d = O.calibrate(x_bits)["d"]
+    codes, s, z, y = O.rotate_quant_int4(x_bits, d, precision="f64")
+    wf = O.fold_weights(w_bits, d)
+    wf_bits = W.f32_to_bf16_bits(wf.astype(np.float32))
+    wfb = O.bf16_bits_to_f64(wf_bits)
+    got = O.int4_linear(codes, s, z, wf_bits)
+    ref = O.bf16_bits_to_f64(x_bits) @ O.bf16_bits_to_f64(w_bits).T
+    bound = (s[:, None] / 2) * np.abs(wfb).sum(axis=1)[None, :] + np.abs(y) @ np.abs(wfb - wf).T
+    assert np.all(np.abs(got - ref) <= bound * (1 + 1e-9) + 1e-12)
+    # and the bound is not vacuous: the product keeps most of the signal
+    assert np.linalg.norm(got - ref) < 0.2 * np.linalg.norm(ref)
