@@ -27,28 +27,40 @@ using wave::bf16x8_t;
 using wave::f32x4_t;
 using wave::u32x4_t;
 
-constexpr int kBM = 128;  // tokens per work-group tile
+constexpr int kBM = 256;  // tokens per work-group tile
 constexpr int kBN = 256;  // weight rows per work-group tile
-constexpr int kBK = 64;   // k per LDS stage
-constexpr int kThreads = 256;
-constexpr int kAStage = kBM * kBK / 2;  // packed codes, 4 KiB
-constexpr int kBStage = kBN * kBK * 2;  // bf16 weights, 32 KiB
-constexpr int kStage = kAStage + kBStage;
+constexpr int kBK = 64;   // k per step
+constexpr int kThreads = 512;
+constexpr int kStages = 4;
+constexpr int kBStage = kBN * kBK * 2;  // one LDS buffer of bf16 weights, 32 KiB
+constexpr int kAStage = kBM * kBK / 2;  // one LDS buffer of packed codes, 8 KiB
+
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 // Eight codes (one dword; code 2i in the low nibble of byte i) -> the eight
-// bf16 values of an MFMA operand, element e = code e.
-__device__ __forceinline__ bf16x8_t widen8(uint32_t c) {
-  const uint32_t lo = c & 0x0F0F0F0Fu;         // codes 0, 2, 4, 6
-  const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;  // codes 1, 3, 5, 7
-  u32x4_t r;
+// bf16 values of an MFMA operand, element e = code e, in two halves so that
+// the conversion can be spread between MFMAs.  Nibbles: codes 0, 2, 4, 6 in
+// the bytes of lo, codes 1, 3, 5, 7 in the bytes of hi.
+struct Nibbles {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Nibbles split_nibbles(uint32_t c) {
+  Nibbles v{c & 0x0F0F0F0Fu, (c >> 4) & 0x0F0F0F0Fu};
+  // hide the known-zero high nibbles, so that each byte goes through one
+  // v_cvt_f32_ubyte{0..3} instead of an extract and a convert
+  asm("" : "+v"(v.lo), "+v"(v.hi));
+  return v;
+}
+// Words 2h and 2h + 1 of the operand: elements 4h .. 4h + 3.
+template <int H>
+__device__ __forceinline__ void widen_half(const Nibbles& v, u32x4_t& r) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float e0 = static_cast<float>((lo >> (8 * i)) & 0xffu);
-    const float e1 = static_cast<float>((hi >> (8 * i)) & 0xffu);
+  for (int i = 2 * H; i < 2 * H + 2; ++i) {
+    const float e0 = static_cast<float>((v.lo >> (8 * i)) & 0xffu);
+    const float e1 = static_cast<float>((v.hi >> (8 * i)) & 0xffu);
     // top halves of the two binary32 values: (bf16(e0), bf16(e1)), exact
     r[i] = __builtin_amdgcn_perm(__float_as_uint(e1), __float_as_uint(e0), 0x07060302u);
   }
-  return __builtin_bit_cast(bf16x8_t, r);
 }
 
 // Block id -> (token tile, row tile).  Consecutive block ids go to different
@@ -70,94 +82,151 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
   tn = r / gm;
 }
 
+// The MFMA's 32 k positions are a free relabelling of channels, as long as
+// both operands use the same one: in k step kt, lane group g (lanes 16 g ..
+// 16 g + 15) takes channels 64 kt + 16 g + 8 kk + (0..7) for MFMA half kk.
+// A lane's codes for both halves are then 8 consecutive bytes, and its
+// weights chunk 2 g + kk of the row's 128-byte k slice.
+//
+// Both operands go global -> LDS by global_load_lds_dwordx4 (lane L of an
+// instruction writes LDS bytes 16 L .. 16 L + 15 above the wave-uniform base),
+// into rings of four buffers; no global load targets registers, so every
+// memory wait in the loop is the explicit one before the barrier.
+//
+// Weights, 32 KiB a step: instruction i of wave w fills LDS rows 32 w + 8 i ..
+// + 7, lane L at row (L >> 3), physical chunk L & 7.  A row is 128 bytes, half
+// of the 64 four-byte banks, and logical chunk c of row r sits at physical
+// chunk c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle serves in a
+// 16-byte operand read (rows r0 .. r0 + 15, one chunk) cover all 64 banks.
+//
+// Codes, 8 KiB a step (256 tokens x 32 bytes): wave w fills token rows
+// 32 w .. + 31; in each 16-row group the first 16 bytes of every row come
+// first (256 bytes), then the second 16 bytes, so the 8-byte reads of 32
+// lanes (16 rows, one half) are one contiguous 256-byte span.
+//
+// Eight waves: wave (wm, wn) owns tokens 64 wm .. + 63 and rows
+// 128 wn .. + 127 of the tile.  Step kt: read this step's second-half codes
+// and the next step's first-half codes from LDS; half 0 (32 MFMAs on the
+// codes widened last step, while half 1's are widened), half 1 (32 MFMAs,
+// while the next step's half 0 is widened); then issue step kt + 3's codes
+// and weights into the buffers step kt - 1 used, wait for step kt + 2's codes
+// (and so for everything older) and pass one barrier.  Weights have two steps
+// to arrive, codes one.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void int4_linear_kernel(LinearArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kBStage + kAStage)];
+  uint8_t* const lds_b = lds;
+  uint8_t* const lds_a = lds + kStages * kBStage;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;  // wave tile: tokens 64*wm.., rows 128*wn..
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid & 3, wn = wid >> 2;
   const int g = lane >> 4, nl = lane & 15;
 
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, a.tiles_m, a.tiles_n, tm, tn);
   const int m0 = tm * kBM, n0 = tn * kBN;
-  const int64_t row_bytes = a.n >> 1;
+  const int ktiles = a.n / kBK;
+  const int last = ktiles - 1;
 
-  // Global -> LDS staging.  Codes: thread -> token row ra, 32 codes (16 B) at
-  // k = 32*ha of the stage.  Weights: thread -> 16-B chunk cb of rows
-  // rb0 + 32 i.  Rows past the end are clamped (their results are not stored).
-  const int ra = tid >> 1, ha = tid & 1;
-  const uint8_t* gA = a.codes + static_cast<int64_t>(min(m0 + ra, a.T - 1)) * row_bytes + 16 * ha;
-  const int cb = tid & 7, rb0 = tid >> 3;
-  int offB[8];
+  // Code source of lane L (rows clamped; their results are not stored):
+  // token row 32 wid + 16 (L >> 5) + (L & 15), bytes 16 ((L >> 4) & 1) of the step
+  const uint32_t row_bytes = static_cast<uint32_t>(a.n) >> 1;
+  const uint32_t offA =
+      static_cast<uint32_t>(min(m0 + 32 * wid + 16 * (lane >> 5) + (lane & 15), a.T - 1)) * row_bytes +
+      16 * ((lane >> 4) & 1);
+  // Weight source of lane L in instruction i (rows clamped); its tile row
+  // 32 wid + 8 i + (L >> 3) has (row >> 1) & 7 = 4 (i & 1) + (L >> 4)
+  uint32_t offB[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) offB[i] = min(n0 + rb0 + 32 * i, a.R - 1) * a.ldw + 8 * cb;
+  for (int i = 0; i < 4; ++i) {
+    const int lchunk = (lane & 7) ^ ((4 * (i & 1) + (lane >> 4)) & 7);
+    offB[i] = static_cast<uint32_t>(min(n0 + 32 * wid + 8 * i + (lane >> 3), a.R - 1)) * a.ldw + 8 * lchunk;
+  }
+  const int b_load = 128 * (128 * wn + nl);  // + 2048 nf; (row >> 1) & 7 = nl >> 1
+  const int b_kk[2] = {16 * ((2 * g) ^ (nl >> 1)), 16 * ((2 * g + 1) ^ (nl >> 1))};
+  // codes of frag mf for this lane: 8 bytes at a_load + 512 mf
+  const int a_load = 2048 * wm + 256 * (g >> 1) + 16 * nl + 8 * (g & 1);
 
-  // LDS layouts.  Codes, per wave-row half wm, in read order: the dword of
-  // (token frag mf, k half kk, lane) at word 512 wm + 256 (mf>>1) + 4 lane +
-  // 2 (mf&1) + kk, so each lane reads its eight dwords with two b128 reads.
-  // Weights: row r (0..255) holds 8 chunks of 16 B, chunk c at c ^ (r & 7).
-  const int rowA_w = ra >> 6, mfA = (ra >> 4) & 3, nlA = ra & 15;
-  const int a_store = 4 * (512 * rowA_w + 256 * (mfA >> 1) + 4 * nlA + 2 * (mfA & 1) + ha);  // + 256 g bytes
-  const int b_store = kAStage + 128 * rb0 + 16 * (cb ^ (rb0 & 7));                         // + 4096 i
-  const int a_load = 2048 * wm + 16 * lane;                                                  // + 1024
-  const int b_load = kAStage + 128 * (128 * wn + nl);                                        // + 2048 nf
-  const int b_chunk = g ^ (nl & 7);                                                          // ^ 4 kk
+  // Every step issues exactly one code and four weight loads per wave
+  // (clamped to the last step at the end), so the vmcnt thresholds are exact.
+  auto issue = [&](int kt) {
+    const int ks = min(kt, last);
+    const int buf = kt & (kStages - 1);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.codes + offA + 32u * ks),
+                                     (__attribute__((address_space(3))) void*)(lds_a + buf * kAStage + 1024 * wid),
+                                     16, 0, 0);
+    const uint16_t* src = a.w + ks * kBK;
+    uint8_t* dst = lds_b + buf * kBStage + 4096 * wid;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + offB[i]),
+                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+  };
+  auto read_codes = [&](int kt, u32x2_t (&dst)[4]) {
+    const uint8_t* src = lds_a + (kt & (kStages - 1)) * kAStage + a_load;
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) dst[mf] = *reinterpret_cast<const u32x2_t*>(src + 512 * mf);
+  };
 
   f32x4_t acc[4][8];
 #pragma unroll
   for (int mf = 0; mf < 4; ++mf)
 #pragma unroll
     for (int nf = 0; nf < 8; ++nf) acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t af[2][4];  // widened codes of half 0 and half 1
 
-  uint4 ra_reg;
-  uint4 rb_reg[8];
-  auto gload = [&](int kt) {
-    ra_reg = *reinterpret_cast<const uint4*>(gA + static_cast<int64_t>(kt) * (kBK / 2));
+  issue(0);
+  issue(1);
+  issue(2);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  {
+    u32x2_t c[4];
+    read_codes(0, c);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      rb_reg[i] = *reinterpret_cast<const uint4*>(a.w + static_cast<int64_t>(offB[i]) + kt * kBK);
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* base = lds + stage * kStage;
-    *reinterpret_cast<uint32_t*>(base + a_store) = ra_reg.x;
-    *reinterpret_cast<uint32_t*>(base + a_store + 256) = ra_reg.y;
-    *reinterpret_cast<uint32_t*>(base + a_store + 512) = ra_reg.z;
-    *reinterpret_cast<uint32_t*>(base + a_store + 768) = ra_reg.w;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(base + b_store + 4096 * i) = rb_reg[i];
-  };
+    for (int mf = 0; mf < 4; ++mf) {
+      const Nibbles v = split_nibbles(c[mf][0]);
+      widen_half<0>(v, af[0][mf]);
+      widen_half<1>(v, af[0][mf]);
+    }
+  }
 
-  const int ktiles = a.n / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int stage = kt & 1;
-    if (kt + 1 < ktiles) gload(kt + 1);
-    const uint8_t* base = lds + stage * kStage;
-    const u32x4_t c01 = *reinterpret_cast<const u32x4_t*>(base + a_load);
-    const u32x4_t c23 = *reinterpret_cast<const u32x4_t*>(base + a_load + 1024);
+  for (int kt = 0; kt <= last; ++kt) {
+    const uint8_t* const sbase = lds_b + (kt & (kStages - 1)) * kBStage;
+    u32x2_t c0[4], c1[4];
+    read_codes(kt, c0);
+    read_codes(kt + 1, c1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[4];
-      af[0] = widen8(c01[kk]);
-      af[1] = widen8(c01[2 + kk]);
-      af[2] = widen8(c23[kk]);
-      af[3] = widen8(c23[2 + kk]);
-      const uint8_t* bb = base + b_load + 16 * (b_chunk ^ (4 * kk));
+      Nibbles v[4];
+      const uint8_t* const bsrc = sbase + b_load + b_kk[kk];
+      u32x4_t bf[8];
+      bf[0] = *reinterpret_cast<const u32x4_t*>(bsrc);
+      bf[1] = *reinterpret_cast<const u32x4_t*>(bsrc + 2048);
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf) {
-        const bf16x8_t bf = *reinterpret_cast<const bf16x8_t*>(bb + 2048 * nf);
+        if (nf + 2 < 8) bf[nf + 2] = *reinterpret_cast<const u32x4_t*>(bsrc + 2048 * (nf + 2));
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf)
-          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mf], bf, acc[mf][nf], 0, 0, 0);
+          acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[kk][mf]),
+                                                                __builtin_bit_cast(bf16x8_t, bf[nf]), acc[mf][nf],
+                                                                0, 0, 0);
+        // one half of one dword per frag column: four dwords over eight columns
+        const int mfw = nf >> 1;
+        const uint32_t src = kk == 0 ? c0[mfw][1] : c1[mfw][0];
+        if ((nf & 1) == 0) {
+          v[mfw] = split_nibbles(src);
+          widen_half<0>(v[mfw], af[kk ^ 1][mfw]);
+        } else {
+          widen_half<1>(v[mfw], af[kk ^ 1][mfw]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (kt + 1 < ktiles) {
-      lstore(stage ^ 1);
-      __syncthreads();
-    }
+    issue(kt + 3);
+    // after step kt + 2's code load (end of step kt - 1) came nine loads:
+    // weights kt + 2, codes kt + 3, weights kt + 3
+    asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
   }
 
   // Epilogue: lane (g, nl) holds tokens 4g + r of each 16-token frag, for
@@ -219,6 +288,7 @@ __global__ void weight_rowsum_kernel(const uint16_t* __restrict__ w, int64_t n, 
 
 bool int4_linear_fast_ok(const LinearArgs& a) {
   return a.n % kBK == 0 && a.ldw % 8 == 0 && static_cast<int64_t>(a.R) * a.ldw < (int64_t{1} << 31) &&
+         static_cast<int64_t>(a.T) * (a.n / 2) < (int64_t{1} << 31) &&
          (reinterpret_cast<uintptr_t>(a.codes) & 15u) == 0 && (reinterpret_cast<uintptr_t>(a.w) & 15u) == 0;
 }
 
