@@ -205,13 +205,15 @@ def bench_linear(args, torch, R, W) -> int:
     flops = 2.0 * t * n * rows
     achieved = flops / (ms * 1e-3) / 1e12
     # context: the library bf16 GEMM (hipBLASLt via torch) on the same shape,
-    # with the activations already dequantized to bf16
+    # alone (activations already dequantized to bf16) and as the unfused
+    # consumer it would be here (dequantize to bf16, then the GEMM)
     yb = R.dequant(codes, scale, zero).to(torch.bfloat16)
     wt = wf.t()
     for _ in range(20):
         torch.matmul(yb, wt)
     _, ms_lib = timed(lambda: torch.matmul(yb, wt), 50)
     del yb
+    _, ms_unfused = timed(lambda: torch.matmul(R.dequant(codes, scale, zero).to(torch.bfloat16), wt), 20)
     line = {
         "metric": "tokens/s and achieved TFLOP/s, INT4-activation down-projection with zero-point correction",
         "value": t * args.steps / wall, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -221,7 +223,8 @@ def bench_linear(args, torch, R, W) -> int:
                                f"times W' [{rows} x {n}] bf16, out f32 [{t} x {rows}]",
                    "kernel": R.int4_linear_kernel_name(codes, wf),
                    "library_bf16_gemm_ms": ms_lib,
-                   "library_bf16_gemm_tflops": flops / (ms_lib * 1e-3) / 1e12},
+                   "library_bf16_gemm_tflops": flops / (ms_lib * 1e-3) / 1e12,
+                   "unfused_dequant_plus_library_gemm_ms": ms_unfused},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None, "flops_per_launch": flops,
                      "kernel_avg_ms": ms},

@@ -12,8 +12,9 @@
 // operand is read from the packed codes and widened to bf16 in registers (the
 // integers 0..15 are exact in bf16), so the codes cross HBM and LDS at 4 bits
 // a value.  B is W' in bf16.  Accumulation is binary32; the epilogue applies
-// scale and zero.  Work-group tile 128 tokens x 256 weight rows x 64 k, four
-// waves of 64 x 128, LDS double-buffered; one barrier per k step.
+// scale and zero.  Work-group tile 256 tokens x 256 weight rows, k steps of
+// 64, eight waves of 64 x 128; both operands stream global -> LDS through
+// four-deep rings; one barrier per k step.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,25 +94,26 @@ __device__ __forceinline__ void tile_of(int bid, int nblocks, int tiles_m, int t
 // into rings of four buffers; no global load targets registers, so every
 // memory wait in the loop is the explicit one before the barrier.
 //
-// Weights, 32 KiB a step: instruction i of wave w fills LDS rows 32 w + 8 i ..
-// + 7, lane L at row (L >> 3), physical chunk L & 7.  A row is 128 bytes, half
-// of the 64 four-byte banks, and logical chunk c of row r sits at physical
-// chunk c ^ ((r >> 1) & 7): the 16 lanes that one LDS cycle serves in a
-// 16-byte operand read (rows r0 .. r0 + 15, one chunk) cover all 64 banks.
+// Weights, 32 KiB a step, [256 rows][8 chunks of 16 bytes]: instruction i of
+// wave w fills rows 32 w + 8 i .. + 7, lane L at row (L >> 3), physical chunk
+// L & 7.  Logical chunk c of row r sits at physical chunk c ^ h(r),
+// h(r) = (r & 7) ^ ((r >> 3) & 1).  An operand read has 16 lanes on 16
+// consecutive rows at one logical chunk; with this h the rocprofv3 counter
+// SQ_LDS_BANK_CONFLICT reads zero for them on gfx950, where no swizzle, or
+// c ^ (r & 7), cost 12 and 4 conflict cycles per read.
 //
 // Codes, 8 KiB a step (256 tokens x 32 bytes): wave w fills token rows
 // 32 w .. + 31; in each 16-row group the first 16 bytes of every row come
-// first (256 bytes), then the second 16 bytes, so the 8-byte reads of 32
-// lanes (16 rows, one half) are one contiguous 256-byte span.
+// first (256 bytes), then the second 16 bytes.  Each lane reads its 8 bytes
+// of a step with one conflict-free 8-byte LDS read.
 //
 // Eight waves: wave (wm, wn) owns tokens 64 wm .. + 63 and rows
-// 128 wn .. + 127 of the tile.  Step kt: read this step's second-half codes
-// and the next step's first-half codes from LDS; half 0 (32 MFMAs on the
-// codes widened last step, while half 1's are widened), half 1 (32 MFMAs,
-// while the next step's half 0 is widened); then issue step kt + 3's codes
-// and weights into the buffers step kt - 1 used, wait for step kt + 2's codes
-// (and so for everything older) and pass one barrier.  Weights have two steps
-// to arrive, codes one.
+// 128 wn .. + 127 of the tile.  Step kt: read the next step's codes from LDS;
+// half 0 (32 MFMAs on the codes widened last step, while half 1's are
+// widened); half 1 (32 MFMAs, while the next step's half 0 is widened, and
+// step kt + 3's codes and weights are issued into the buffers step kt - 1
+// used); then wait for step kt + 2's codes (and so for everything older) and
+// pass one barrier.  Weights have two steps to arrive, codes one and a half.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void int4_linear_kernel(LinearArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * (kBStage + kAStage)];
@@ -135,38 +137,45 @@ void int4_linear_kernel(LinearArgs a) {
   const uint32_t offA =
       static_cast<uint32_t>(min(m0 + 32 * wid + 16 * (lane >> 5) + (lane & 15), a.T - 1)) * row_bytes +
       16 * ((lane >> 4) & 1);
-  // Weight source of lane L in instruction i (rows clamped); its tile row
-  // 32 wid + 8 i + (L >> 3) has (row >> 1) & 7 = 4 (i & 1) + (L >> 4)
+  // Weight source of lane L in instruction i (rows clamped): tile row r =
+  // 32 wid + 8 i + (L >> 3), logical chunk (L & 7) ^ h(r)
+  auto h = [](int r) { return (r & 7) ^ ((r >> 3) & 1); };
   uint32_t offB[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int lchunk = (lane & 7) ^ ((4 * (i & 1) + (lane >> 4)) & 7);
-    offB[i] = static_cast<uint32_t>(min(n0 + 32 * wid + 8 * i + (lane >> 3), a.R - 1)) * a.ldw + 8 * lchunk;
+    const int r = 32 * wid + 8 * i + (lane >> 3);
+    offB[i] = static_cast<uint32_t>(min(n0 + r, a.R - 1)) * a.ldw + 8 * ((lane & 7) ^ h(r));
   }
-  const int b_load = 128 * (128 * wn + nl);  // + 2048 nf; (row >> 1) & 7 = nl >> 1
-  const int b_kk[2] = {16 * ((2 * g) ^ (nl >> 1)), 16 * ((2 * g + 1) ^ (nl >> 1))};
+  // operand rows 128 wn + 16 nf + nl: h depends on nl only
+  const int b_load = 128 * (128 * wn + nl);  // + 2048 nf
+  const int b_kk[2] = {16 * ((2 * g) ^ h(nl)), 16 * ((2 * g + 1) ^ h(nl))};
   // codes of frag mf for this lane: 8 bytes at a_load + 512 mf
   const int a_load = 2048 * wm + 256 * (g >> 1) + 16 * nl + 8 * (g & 1);
 
   // Every step issues exactly one code and four weight loads per wave
   // (clamped to the last step at the end), so the vmcnt thresholds are exact.
-  auto issue = [&](int kt) {
+  // Load j of step kt: j = 0 the codes, j = 1..4 the weights.
+  auto issue_one = [&](int kt, int j) {
     const int ks = min(kt, last);
     const int buf = kt & (kStages - 1);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.codes + offA + 32u * ks),
-                                     (__attribute__((address_space(3))) void*)(lds_a + buf * kAStage + 1024 * wid),
-                                     16, 0, 0);
-    const uint16_t* src = a.w + ks * kBK;
-    uint8_t* dst = lds_b + buf * kBStage + 4096 * wid;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + offB[i]),
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * i), 16, 0, 0);
+    if (j == 0) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(a.codes + offA + 32u * ks),
+                                       (__attribute__((address_space(3))) void*)(lds_a + buf * kAStage + 1024 * wid),
+                                       16, 0, 0);
+    } else {
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(a.w + ks * kBK + offB[j - 1]),
+          (__attribute__((address_space(3))) void*)(lds_b + buf * kBStage + 4096 * wid + 1024 * (j - 1)), 16, 0, 0);
+    }
   };
   auto read_codes = [&](int kt, u32x2_t (&dst)[4]) {
     const uint8_t* src = lds_a + (kt & (kStages - 1)) * kAStage + a_load;
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) dst[mf] = *reinterpret_cast<const u32x2_t*>(src + 512 * mf);
+    for (int mf = 0; mf < 4; ++mf) {
+      dst[mf] = *reinterpret_cast<const u32x2_t*>(src + 512 * mf);
+      // both dwords are used (one now, one a step later): keep the read 8 bytes wide
+      asm("" : "+v"(dst[mf]));
+    }
   };
 
   f32x4_t acc[4][8];
@@ -176,25 +185,22 @@ void int4_linear_kernel(LinearArgs a) {
     for (int nf = 0; nf < 8; ++nf) acc[mf][nf] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t af[2][4];  // widened codes of half 0 and half 1
 
-  issue(0);
-  issue(1);
-  issue(2);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  {
-    u32x2_t c[4];
-    read_codes(0, c);
 #pragma unroll
-    for (int mf = 0; mf < 4; ++mf) {
-      const Nibbles v = split_nibbles(c[mf][0]);
-      widen_half<0>(v, af[0][mf]);
-      widen_half<1>(v, af[0][mf]);
-    }
+  for (int j = 0; j < 15; ++j) issue_one(j / 5, j % 5);
+  wave::wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  u32x2_t c0[4];  // codes of the current step
+  read_codes(0, c0);
+#pragma unroll
+  for (int mf = 0; mf < 4; ++mf) {
+    const Nibbles v = split_nibbles(c0[mf][0]);
+    widen_half<0>(v, af[0][mf]);
+    widen_half<1>(v, af[0][mf]);
   }
 
   for (int kt = 0; kt <= last; ++kt) {
     const uint8_t* const sbase = lds_b + (kt & (kStages - 1)) * kBStage;
-    u32x2_t c0[4], c1[4];
-    read_codes(kt, c0);
+    u32x2_t c1[4];  // codes of the next step
     read_codes(kt + 1, c1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -206,6 +212,8 @@ void int4_linear_kernel(LinearArgs a) {
 #pragma unroll
       for (int nf = 0; nf < 8; ++nf) {
         if (nf + 2 < 8) bf[nf + 2] = *reinterpret_cast<const u32x4_t*>(bsrc + 2048 * (nf + 2));
+        // step kt + 3's loads, spread over the second half
+        if (kk == 1 && nf < 5) issue_one(kt + 3, nf);
 #pragma unroll
         for (int mf = 0; mf < 4; ++mf)
           acc[mf][nf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[kk][mf]),
@@ -223,10 +231,12 @@ void int4_linear_kernel(LinearArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    issue(kt + 3);
-    // after step kt + 2's code load (end of step kt - 1) came nine loads:
-    // weights kt + 2, codes kt + 3, weights kt + 3
-    asm volatile("s_waitcnt vmcnt(9)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int mf = 0; mf < 4; ++mf) c0[mf] = c1[mf];
+    // after step kt + 2's code load (second half of step kt - 1) came nine
+    // loads: weights kt + 2, codes kt + 3, weights kt + 3
+    wave::wait_vmcnt<9>();
+    __builtin_amdgcn_s_barrier();
   }
 
   // Epilogue: lane (g, nl) holds tokens 4g + r of each 16-token frag, for
