@@ -15,9 +15,10 @@ The inputs are copied to several device buffers whose total exceeds the
 step reads its input from HBM.
 
 Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
---warmup W, --no-cpu-baseline, --no-decode (skip the decode-latency leg),
---pmc-copy (also run plain copies of known size for the counter calibration
-of a rocprofv3 --pmc run).
+--warmup W, --workload W, --no-cpu-baseline, --no-decode (skip the
+decode-latency leg), --pmc-copy (also run plain copies of known size for the
+counter calibration of a rocprofv3 --pmc run); --fold times the offline weight
+fold and --linear the INT4-activation down-projection instead.
 """
 
 from __future__ import annotations
