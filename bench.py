@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of SignRot's fused online path on one MI355X.
 
-One step = one call of signrot_rotate_quant_int4 over a whole batch: bf16
+One step = one call of signrot_rotate_quant_int4_outlier (the online path
+with the calibrated sign vector d = sigma * row c of H, passed as (c, sigma))
+over a whole batch: bf16
 activations in HBM -> Hadamard rotation -> sign flip -> per-token min/max ->
 scale, zero-point -> rounding -> packed int4 codes in HBM.  Calibration is an
 offline step and is not timed.
@@ -282,13 +284,13 @@ def workload_text(w, n: int, t: int, c: int) -> str:
             f"calibration on {cal}")
 
 
-def decode_latency(R, W, torch, d, calls: int = 10000) -> dict:
+def decode_latency(R, W, torch, c, sigma, calls: int = 10000) -> dict:
     """Latency of decode-shaped calls (1, 4, 16 tokens of the n = 14336 law):
     microseconds per call for back-to-back launches and for one HIP graph
     holding `calls` launches.  The graph's output is checked against an eager
     call on the same input after every replay."""
     out = {}
-    fn = R.lib().signrot_rotate_quant_int4
+    fn = R.lib().signrot_rotate_quant_int4_outlier
     for t in (1, 4, 16):
         bits, _ = W.decode_batch("cfg5", t, 0)
         n = bits.shape[1]
@@ -296,13 +298,13 @@ def decode_latency(R, W, torch, d, calls: int = 10000) -> dict:
         co = torch.empty((t, n // 2), dtype=torch.uint8, device="cuda")
         sc = torch.empty(t, dtype=torch.float32, device="cuda")
         ze = torch.empty(t, dtype=torch.float32, device="cuda")
-        ref = R.rotate_quant_int4(x, d)
+        ref = R.rotate_quant_int4_outlier(x, c, sigma)
 
         def launch(stream):
-            st = fn(x.data_ptr(), t, n, n, d.data_ptr(), co.data_ptr(), sc.data_ptr(), ze.data_ptr(), None,
+            st = fn(x.data_ptr(), t, n, n, c, sigma, co.data_ptr(), sc.data_ptr(), ze.data_ptr(), None,
                     ctypes.c_void_p(stream.cuda_stream))
             if st != 0:
-                R.check(st, "signrot_rotate_quant_int4")
+                R.check(st, "signrot_rotate_quant_int4_outlier")
 
         stream = torch.cuda.current_stream()
         for _ in range(100):
@@ -385,7 +387,8 @@ def main() -> int:
     bits, meta = W.batch(wname, tokens=args.tokens)
     t, n = bits.shape
     x0 = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    d, c, _, _ = R.calibrate(to_dev_bits(W.calibration_batch(wname)[0], torch))
+    d, c, _, mc = R.calibrate(to_dev_bits(W.calibration_batch(wname)[0], torch))
+    sigma = -1 if mc < 0 else 1
 
     in_bytes = x0.numel() * 2
     nsets = max(2, int(np.ceil(BUFFER_SETS_MIN_BYTES / in_bytes)))
@@ -395,17 +398,20 @@ def main() -> int:
              torch.empty(t, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
+    # the step: the calibrated sign vector d = sigma * (row c of H), passed as
+    # (c, sigma); the same computation through the d-vector entry point is
+    # timed after it for reference
     calls = []
     for i in range(nsets):
         co, sc, ze = outs[i]
-        calls.append((xs[i].data_ptr(), t, n, n, d.data_ptr(), co.data_ptr(), sc.data_ptr(), ze.data_ptr(),
+        calls.append((xs[i].data_ptr(), t, n, n, c, sigma, co.data_ptr(), sc.data_ptr(), ze.data_ptr(),
                       None, sptr))
-    fn = L.signrot_rotate_quant_int4
+    fn = L.signrot_rotate_quant_int4_outlier
 
     def step(i):
         st = fn(*calls[i % nsets])
         if st != 0:
-            R.check(st, "signrot_rotate_quant_int4")
+            R.check(st, "signrot_rotate_quant_int4_outlier")
 
     for i in range(args.warmup):
         step(i)
@@ -424,6 +430,21 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # reference: the same steps through the d-vector entry point
+    dcalls = [(xs[i].data_ptr(), t, n, n, d.data_ptr(), outs[i][0].data_ptr(), outs[i][1].data_ptr(),
+               outs[i][2].data_ptr(), None, sptr) for i in range(nsets)]
+    ev2 = torch.cuda.Event(enable_timing=True)
+    ev3 = torch.cuda.Event(enable_timing=True)
+    dsteps = min(args.steps, 200)
+    ev2.record(stream)
+    for i in range(dsteps):
+        st = L.signrot_rotate_quant_int4(*dcalls[i % nsets])
+        if st != 0:
+            R.check(st, "signrot_rotate_quant_int4")
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    dvec_ms = ev2.elapsed_time(ev3) / dsteps
 
     if args.pmc_copy:
         # plain copies of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
@@ -460,6 +481,8 @@ def main() -> int:
             "tokens": t,
             "parallelism": "single GPU",
             "kernel": kname,
+            "entry_point": "signrot_rotate_quant_int4_outlier (d = sigma * row c of H, from calibration)",
+            "d_vector_entry_point_kernel_avg_ms": dvec_ms,
             "input_buffer_sets": nsets,
             "hbm_gbs_wall": bpt * tokens_per_s / 1e9,
             "pct_of_peak_hbm_wall": 100.0 * bpt * tokens_per_s / 1e9 / PEAK_HBM_GBS,
@@ -479,7 +502,7 @@ def main() -> int:
     }
     if not args.no_decode and n == 14336:
         line["decode"] = {"workload": "n=14336, 1/4/16 tokens per call, same law; 10^4 calls",
-                          "tokens": decode_latency(R, W, torch, d)}
+                          "tokens": decode_latency(R, W, torch, c, sigma)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy())
     print(json.dumps(line), flush=True)

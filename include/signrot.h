@@ -118,6 +118,28 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
                               float* y_out, void* stream);
 
 /*
+ * The online path for the sign vector in its calibrated form, given by the
+ * outlier channel c and sigma = sign(M_c) instead of as the vector d
+ * (explainer, paragraph on the sign adjustment: each column j of H is
+ * multiplied by the sign of the outlier row's entry, so d_j = sigma * H[c][j]
+ * with H the library's unnormalised +-1 matrix).  Computes exactly what
+ * signrot_rotate_quant_int4 computes for that d, without reading d or
+ * deciding its form on the device, which saves a few microseconds per call.
+ *
+ *   c       the channel signrot_calibrate returns in c_out, 0 <= c < n.
+ *   sigma   +1 or -1: the sign of M_c (mc_out), with sign(+-0) = +1.
+ *   the other arguments as for signrot_rotate_quant_int4.
+ *
+ * c outside [0, n) or sigma not +-1 -> SIGNROT_EINVAL; the other errors as
+ * for signrot_rotate_quant_int4.  For the widths without a fast kernel, d is
+ * built in a stream-ordered n-byte scratch (hipMallocAsync / hipFreeAsync).
+ * Asynchronous.
+ */
+int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c,
+                                      int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
+                                      void* stream);
+
+/*
  * Dequantization: y_hat[t][j] = scale[t] * (q_j - zero[t]), the level value
  * of each code (mn + q * scale).  codes/scale/zero as produced above; y_hat
  * device [tokens][n] float.  n must be supported.  Asynchronous.

@@ -47,6 +47,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_calibrate.restype = ctypes.c_int
     L.signrot_rotate_quant_int4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     L.signrot_rotate_quant_int4.restype = ctypes.c_int
+    L.signrot_rotate_quant_int4_outlier.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    L.signrot_rotate_quant_int4_outlier.restype = ctypes.c_int
     L.signrot_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
     L.signrot_dequant.restype = ctypes.c_int
     L.signrot_fold_weights.argtypes = [vp, i64, i64, i64, vp, vp, vp]
@@ -73,6 +75,7 @@ EXPORTED = (
     "signrot_supported_n",
     "signrot_calibrate",
     "signrot_rotate_quant_int4",
+    "signrot_rotate_quant_int4_outlier",
     "signrot_dequant",
     "signrot_fold_weights",
     "signrot_weight_rowsum",
@@ -162,6 +165,27 @@ def signrot_rotate_quant_int4(x, d, y_out: bool = False, out=None):
     return (codes, scale, zero, y) if y is not None else (codes, scale, zero)
 
 
+def signrot_rotate_quant_int4_outlier(x, c: int, sigma: int, y_out: bool = False, out=None):
+    """Like signrot_rotate_quant_int4 for d = sigma * (row c of H), given as the
+    outlier channel c and sigma = sign(M_c) (what signrot_calibrate returns)."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    if out is None:
+        codes = torch.empty((t, n // 2), dtype=torch.uint8, device=x.device)
+        scale = torch.empty(t, dtype=torch.float32, device=x.device)
+        zero = torch.empty(t, dtype=torch.float32, device=x.device)
+        y = torch.empty((t, n), dtype=torch.float32, device=x.device) if y_out else None
+    else:
+        codes, scale, zero = out[:3]
+        y = out[3] if len(out) > 3 else None
+    check(lib().signrot_rotate_quant_int4_outlier(ptr, t, n, ld, int(c), int(sigma), codes.data_ptr(),
+                                                  scale.data_ptr(), zero.data_ptr(),
+                                                  y.data_ptr() if y is not None else None, _stream_of(x)),
+          "signrot_rotate_quant_int4_outlier")
+    return (codes, scale, zero, y) if y is not None else (codes, scale, zero)
+
+
 def signrot_dequant(codes, scale, zero, n: int | None = None):
     """codes u8 [T, n/2], scale/zero f32 [T] -> y_hat f32 [T, n]."""
     import torch
@@ -237,6 +261,7 @@ def int4_linear_kernel_name(codes, w) -> str | None:
 # short aliases
 calibrate = signrot_calibrate
 rotate_quant_int4 = signrot_rotate_quant_int4
+rotate_quant_int4_outlier = signrot_rotate_quant_int4_outlier
 dequant = signrot_dequant
 fold_weights = signrot_fold_weights
 weight_rowsum = signrot_weight_rowsum

@@ -183,6 +183,66 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   return SIGNROT_OK;
 }
 
+int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c,
+                                      int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
+                                      void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  if (!sh.ok) {
+    set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (c < 0 || c >= n) return fail_einval("c must be a channel in [0, n)");
+  if (sigma != 1 && sigma != -1) return fail_einval("sigma must be +1 or -1");
+  if (tokens < 0) return fail_einval("tokens < 0");
+  if (ld < n) return fail_einval("ld < n");
+  if (ld & 7) return fail_einval("ld must be a multiple of 8");
+  if (tokens == 0) return SIGNROT_OK;
+  if (tokens > (int64_t{1} << 40)) return fail_einval("tokens too large");
+  if (!x_bf16 || !codes || !scale || !zero) return fail_einval("null device pointer");
+  if (!aligned16(x_bf16)) return fail_einval("x must be 16-byte aligned");
+  if (!aligned16(codes)) return fail_einval("codes must be 16-byte aligned");
+  if (y_out && !aligned16(y_out)) return fail_einval("y_out must be 16-byte aligned");
+  RqArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = static_cast<const uint16_t*>(x_bf16);
+  a.codes = codes;
+  a.scale = scale;
+  a.zero = zero;
+  a.yout = y_out;
+  a.tokens = tokens;
+  a.ld = ld;
+  a.n = sh.n;
+  a.k = sh.k;
+  a.m28 = sh.m28 ? 1 : 0;
+  a.inv_sqrt_n = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
+  a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
+  a.form_given = 1;
+  a.form_c = static_cast<int>(c);
+  a.form_neg = sigma < 0 ? 1 : 0;
+  for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rq_fast_supports(sh.n, sh.k, sh.m28)) {
+    const hipError_t e = launch_rq_fast(a, st);
+    if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4_outlier launch");
+    return SIGNROT_OK;
+  }
+  // the general kernel reads d: build it in a stream-ordered scratch
+  int8_t* d = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&d), (static_cast<size_t>(n) + 15) & ~size_t{15}, st);
+  if (e != hipSuccess) return fail_hip(e, "hipMallocAsync");
+  e = launch_sign_fill(sh, a.form_c, a.form_neg, d, st);
+  if (e == hipSuccess) {
+    a.d = d;
+    a.form_given = 0;
+    e = launch_rq_generic(a, st);
+  }
+  const hipError_t ef = hipFreeAsync(d, st);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4_outlier launch");
+  return SIGNROT_OK;
+}
+
 int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,
                          void* stream) {
   g_last_error[0] = '\0';

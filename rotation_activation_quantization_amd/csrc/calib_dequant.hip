@@ -70,6 +70,17 @@ __global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int
   if (blockIdx.x == 0 && threadIdx.x == 0) scratch[1] = mbits;
 }
 
+// d[j] = sigma * H[c][j] for a given (c, sigma): the same entries as the
+// calibration fill.
+__global__ void sign_fill_kernel(int n, int k, int m28, H28Masks masks, int c, int neg, int8_t* d) {
+  const int bmask = (1 << k) - 1;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
+    if (m28) bit ^= (masks.m[c >> k] >> (j >> k)) & 1u;
+    d[j] = (bit ^ static_cast<uint32_t>(neg)) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
+  }
+}
+
 // y[t][j] = scale[t] * (q - zero[t]); one thread per code byte.
 __global__ void dequant_kernel(const uint8_t* codes, const float* scale, const float* zero,
                                int64_t tokens, int n, float* y) {
@@ -119,6 +130,14 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float*
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(dequant_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, codes, scale,
                      zero, tokens, n, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_sign_fill(const Shape& sh, int c, int neg, int8_t* d, hipStream_t s) {
+  H28Masks masks;
+  for (int i = 0; i < 28; ++i) masks.m[i] = h28().rowmask[i];
+  const int blocks = (sh.n + 255) / 256;
+  hipLaunchKernelGGL(sign_fill_kernel, dim3(blocks), dim3(256), 0, s, sh.n, sh.k, sh.m28 ? 1 : 0, masks, c, neg, d);
   return hipGetLastError();
 }
 

@@ -44,6 +44,9 @@ struct RqArgs {
   int m28;
   float inv_sqrt_n;    // binary32(1 / sqrt(n))
   float inv_15sqrt_n;  // binary32(1 / (15 sqrt(n)))
+  int form_given;      // 1: d = sigma * (row form_c of H) is given by (form_c, form_neg); d unused
+  int form_c;
+  int form_neg;        // 1 when sigma = -1
   uint32_t h28mask[28];
 };
 
@@ -56,6 +59,8 @@ const char* rq_fast_name(int n);
 
 hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
                             int8_t* d_out, unsigned long long* scratch, hipStream_t s);
+// d[j] = sigma * H[c][j] as int8 +-1 (the calibrated form from (c, sigma)).
+hipError_t launch_sign_fill(const Shape& sh, int c, int neg, int8_t* d, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float* zero,
                           int64_t tokens, int n, float* y, hipStream_t s);
 

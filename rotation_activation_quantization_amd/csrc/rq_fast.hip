@@ -104,40 +104,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int cbq_hi = cb >> (2 + S::LG);
   const int sig = (!GENERAL && form.neg) ? -1 : 1;
 
-  // MFMA weights, A operand: lane (g, nl) holds A[m = nl][k = 8 g + i] with
-  // m -> (a' = 4 w + (nl >> 2), c = nl & 3), k -> (a = 8 kc + 2 g + (i >> 2), bb = i & 3).
-  bf16x8_t wA[S::NKC];
-  {
-    const int ap = 4 * w + (nl >> 2);
-    const int cc = nl & 3;
-    const int hrow = hka_sign<KA>(h28, ca, ap) * sig;
-#pragma unroll
-    for (int kc = 0; kc < S::NKC; ++kc)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ar = 8 * kc + 2 * g + (i >> 2);
-        const int bb = i & 3;
-        int wv = 0;
-        if (ar < KA) {
-          wv = hrow * hka_sign<KA>(h28, ar, ap);
-          if (__popc(static_cast<uint32_t>((bb ^ cbb) & cc)) & 1) wv = -wv;
-        }
-        wA[kc][i] = static_cast<short>(bf16_of_sign(wv));
-      }
-  }
-
-  const float gdpp0 = (((nl >> 0) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
-  const float gdpp1 = (((nl >> 1) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
-  const float gdpp2 = ((nl >> 2) & 1) ? -1.0f : 1.0f;
-  const float gdpp3 = ((nl >> 3) & 1) ? -1.0f : 1.0f;
-
-  // Operand reads: lane (g, nl) of tile t reads pair 4 kc + g, logical quad
-  // NT (nl ^ kXLane) + t, i.e. stored quad q = NT (nl ^ kXLane ^ cbq_hi) + (t ^ cbq_lo).
-  // Its slot offset 256 u + 16 (v ^ u SWZ) (u = q % NT, v = q / NT) equals
-  // (16 v) ^ (KMUL u), so the address of tile t is rbase ^ (KMUL t).
-  const uint32_t rbase = static_cast<uint32_t>(S::PB) * static_cast<uint32_t>(g) +
-                         ((16u * static_cast<uint32_t>(nl ^ kXLane ^ cbq_hi)) ^ (S::KMUL * static_cast<uint32_t>(cbq_lo)));
-
   // Staging: chunk unit s = w + W i (i < CPT) of 64 chunks; lane L takes the
   // a-row of parity L & 1 and chunk index e = L >> 1 inside the unit.  With
   // CR >= 32 chunks per a-row a pair-row spans CR / 32 units; otherwise a
@@ -175,6 +141,52 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       return S::PB * s * (32u / S::CR);
     }
   };
+  u32x4_t st[S::CPT];
+  auto load_row = [&](int64_t r) {
+    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(a.x + r * a.ld);
+#pragma unroll
+    for (int i = 0; i < S::CPT; ++i) st[i] = *reinterpret_cast<const u32x4_t*>(rowp + unit_g(i) + gl);
+  };
+  // The first row's loads go out before the weights are built (all but the
+  // 56-row shape, whose registers are short), so their latency overlaps the
+  // set-up; that matters most for a few tokens per call.
+  constexpr bool kEarlyLoad = (KA != 56);
+  if (kEarlyLoad && static_cast<int64_t>(blockIdx.x) < a.tokens) load_row(blockIdx.x);
+
+  // MFMA weights, A operand: lane (g, nl) holds A[m = nl][k = 8 g + i] with
+  // m -> (a' = 4 w + (nl >> 2), c = nl & 3), k -> (a = 8 kc + 2 g + (i >> 2), bb = i & 3).
+  bf16x8_t wA[S::NKC];
+  {
+    const int ap = 4 * w + (nl >> 2);
+    const int cc = nl & 3;
+    const int hrow = hka_sign<KA>(h28, ca, ap) * sig;
+#pragma unroll
+    for (int kc = 0; kc < S::NKC; ++kc)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ar = 8 * kc + 2 * g + (i >> 2);
+        const int bb = i & 3;
+        int wv = 0;
+        if (ar < KA) {
+          wv = hrow * hka_sign<KA>(h28, ar, ap);
+          if (__popc(static_cast<uint32_t>((bb ^ cbb) & cc)) & 1) wv = -wv;
+        }
+        wA[kc][i] = static_cast<short>(bf16_of_sign(wv));
+      }
+  }
+
+  const float gdpp0 = (((nl >> 0) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
+  const float gdpp1 = (((nl >> 1) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
+  const float gdpp2 = ((nl >> 2) & 1) ? -1.0f : 1.0f;
+  const float gdpp3 = ((nl >> 3) & 1) ? -1.0f : 1.0f;
+
+  // Operand reads: lane (g, nl) of tile t reads pair 4 kc + g, logical quad
+  // NT (nl ^ kXLane) + t, i.e. stored quad q = NT (nl ^ kXLane ^ cbq_hi) + (t ^ cbq_lo).
+  // Its slot offset 256 u + 16 (v ^ u SWZ) (u = q % NT, v = q / NT) equals
+  // (16 v) ^ (KMUL u), so the address of tile t is rbase ^ (KMUL t).
+  const uint32_t rbase = static_cast<uint32_t>(S::PB) * static_cast<uint32_t>(g) +
+                         ((16u * static_cast<uint32_t>(nl ^ kXLane ^ cbq_hi)) ^ (S::KMUL * static_cast<uint32_t>(cbq_lo)));
+
   // The thread and chunk that hold x_c (structured d only).
   int xc_wave = -1, xc_lane = 0, xc_i = 0, xc_e = 0;
   if (!GENERAL) {
@@ -204,12 +216,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int64_t tokens = a.tokens;
   const int64_t grid = gridDim.x;
 
-  u32x4_t st[S::CPT];
-  auto load_row = [&](int64_t r) {
-    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(a.x + r * a.ld);
-#pragma unroll
-    for (int i = 0; i < S::CPT; ++i) st[i] = *reinterpret_cast<const u32x4_t*>(rowp + unit_g(i) + gl);
-  };
   auto write_row = [&](uint32_t bo, int xslot) {
     if (xc_thread) {
 #pragma unroll
@@ -239,7 +245,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   int64_t nxt = cur + grid;
   int64_t nn = nxt + grid;
   if (cur >= tokens) return;
-  load_row(cur);
+  if (!kEarlyLoad) load_row(cur);
   wait_vmcnt<0>();
   write_row(0u, 0);
   if (nxt < tokens) load_row(nxt);
@@ -417,9 +423,16 @@ void rq_fast_kernel(RqArgs a) {
       *reinterpret_cast<u32x4_t*>(lds + 2 * S::kRowBytes + o) = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  build_dbits(a.d, a.n, dbits);  // bit j set when d_j = -1
-  __syncthreads();
-  const DForm form = decode_d_form_fast(a, dbits, h28_lds, scratch);
+  DForm form;
+  if (a.form_given) {
+    // d = sigma * (row c of H) by construction: nothing to read or decode
+    __syncthreads();
+    form = DForm{1, a.form_c, a.form_neg};
+  } else {
+    build_dbits(a.d, a.n, dbits);  // bit j set when d_j = -1
+    __syncthreads();
+    form = decode_d_form_fast(a, dbits, h28_lds, scratch);
+  }
   if (form.structured) rq_fast_body<KA, KB, false, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
   else rq_fast_body<KA, KB, true, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
 }

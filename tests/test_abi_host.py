@@ -175,3 +175,20 @@ def test_int4_linear_kernel_choice(L):
     assert name(codes=FAKE + 8) == "int4_linear_simple"
     assert name(rows=1 << 20, n=4096, ldw=4096) == "int4_linear_simple"  # rows * ldw >= 2^31
     assert name(n=7) is None
+
+
+def test_rotate_quant_outlier_argument_errors(L):
+    def rq(x=FAKE, t=4, n=4096, ld=4096, c=5, sigma=1, codes=FAKE, scale=FAKE, zero=FAKE, y=None):
+        return L.signrot_rotate_quant_int4_outlier(x, t, n, ld, c, sigma, codes, scale, zero, y, None)
+
+    assert rq(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert rq(c=-1) == R.SIGNROT_EINVAL
+    assert rq(c=4096) == R.SIGNROT_EINVAL
+    assert rq(sigma=0) == R.SIGNROT_EINVAL
+    assert rq(sigma=2) == R.SIGNROT_EINVAL
+    assert rq(t=-1) == R.SIGNROT_EINVAL
+    assert rq(ld=4095) == R.SIGNROT_EINVAL
+    assert rq(x=None) == R.SIGNROT_EINVAL
+    assert rq(codes=FAKE + 8) == R.SIGNROT_EINVAL
+    assert rq(y=FAKE + 4) == R.SIGNROT_EINVAL
+    assert rq(t=0, x=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK

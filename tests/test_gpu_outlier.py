@@ -1,0 +1,62 @@
+"""The calibrated-form entry point signrot_rotate_quant_int4_outlier (d given
+as the outlier channel c and sigma) against the oracle, and bit for bit against
+signrot_rotate_quant_int4 called with the same d as a vector."""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import rotation_activation_quantization_amd as R  # noqa: E402
+import signrot_workloads as W  # noqa: E402
+from parity import compare, expected  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits):
+    """bf16 rows on the GPU with the row stride padded to a multiple of 8."""
+    t, n = bits.shape
+    ld = (n + 7) // 8 * 8
+    buf = np.zeros((max(t, 1), ld), np.uint16)
+    buf[:t, :n] = bits
+    return torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)[:t, :n]
+
+
+@pytest.mark.parametrize("n,t", [(4096, 70), (8192, 33), (14336, 45), (28672, 20), (28, 9), (1792, 17), (64, 5),
+                                 (16384, 3)])
+def test_outlier_form_matches_vector_form_and_oracle(n, t):
+    g = np.random.default_rng([61, n])
+    for c, sigma in ((0, 1), (n - 1, -1), (int(g.integers(n)), -1), (int(g.integers(n)), 1)):
+        bits = W.random_rows(t, n, seed=int(c), scale=0.8, outlier=900.0 * sigma)  # outlier on channel c
+        d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+        say(f"[gpu] outlier form n={n} T={t} c={c} sigma={sigma} kernel={R.kernel_name(n)}")
+        x = dev(bits)
+        a = R.rotate_quant_int4_outlier(x, c, sigma, y_out=True)
+        b = R.rotate_quant_int4(x, torch.from_numpy(d).cuda(), y_out=True)
+        torch.cuda.synchronize()
+        a = [v.cpu().numpy() for v in a]
+        b = [v.cpu().numpy() for v in b]
+        for u, v, name in zip(a, b, ("codes", "scale", "zero", "y")):
+            assert np.array_equal(u, v), name
+        compare(expected(bits, d), a[0], a[1], a[2], a[3], label=f"outlier n={n} c={c}")
+
+
+def test_outlier_form_on_the_workload_with_calibrated_c_and_sigma():
+    """(c, sigma) straight from signrot_calibrate on the n = 14336 workload."""
+    cal, _ = W.calibration_batch("target")
+    bits, _ = W.batch("target", tokens=512)
+    d, c, _, m = R.calibrate(dev(cal))
+    sigma = -1 if m < 0 else 1
+    codes, scale, zero = R.rotate_quant_int4_outlier(dev(bits), c, sigma)
+    ref = R.rotate_quant_int4(dev(bits), d)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, ref[0]) and torch.equal(scale, ref[1]) and torch.equal(zero, ref[2])
