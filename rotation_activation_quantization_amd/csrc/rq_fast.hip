@@ -1,7 +1,7 @@
 // Fused rotate + sign flip + per-token asymmetric INT4 for gfx950: the fast
-// kernels for n = 28 * 2^9 (14336, the LLaMA3-8B down-projection input; seven
-// waves per token row), n = 56 * 2^9 (28672, the LLaMA3-70B one; fourteen
-// waves) and n = 2^12, 2^13 (eight waves).
+// kernels for n = 28 * 2^k, k = 7..9 (3584, 7168, 14336 -- the LLaMA3-8B
+// down-projection input; seven waves per token row), n = 56 * 2^9 (28672, the
+// LLaMA3-70B one; fourteen waves) and n = 2^12, 2^13, 2^14 (eight waves).
 //
 // Index split.  A row x[i], i = a * 2^KB + b (a < KA, b < 2^KB), is read as
 // quads: b = 4 q + bb (q < NQ = 2^(KB-2), bb < 4).  The transform
@@ -464,18 +464,27 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool rq_fast_supports(int n, int k, bool m28) {
-  return (m28 && k == 9 && n == 14336) || (m28 && k == 10 && n == 28672) || (!m28 && (n == 4096 || n == 8192));
+  if (m28) return k >= 7 && k <= 10 && n == (28 << k);  // 3584, 7168, 14336, 28672
+  return n == 4096 || n == 8192 || n == 16384;
 }
 
 hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s) {
-  if (a.m28) return a.n == 28672 ? launch_shape<56, 9>(a, s) : launch_shape<28, 9>(a, s);
+  if (a.m28) {
+    switch (a.k) {
+      case 7: return launch_shape<28, 7>(a, s);
+      case 8: return launch_shape<28, 8>(a, s);
+      case 9: return launch_shape<28, 9>(a, s);
+      default: return launch_shape<56, 9>(a, s);  // 28 * 2^10 read as 56 * 2^9
+    }
+  }
   if (a.n == 4096) return launch_shape<32, 7>(a, s);
-  return launch_shape<32, 8>(a, s);
+  if (a.n == 8192) return launch_shape<32, 8>(a, s);
+  return launch_shape<32, 9>(a, s);
 }
 
 const char* rq_fast_name(int n) {
-  if (n == 14336) return "rq_mfma28_w7";
   if (n == 28672) return "rq_mfma56_w14";
+  if (n % 28 == 0) return "rq_mfma28_w7";
   return "rq_mfma32_w8";
 }
 

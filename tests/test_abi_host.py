@@ -192,3 +192,19 @@ def test_rotate_quant_outlier_argument_errors(L):
     assert rq(codes=FAKE + 8) == R.SIGNROT_EINVAL
     assert rq(y=FAKE + 4) == R.SIGNROT_EINVAL
     assert rq(t=0, x=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK
+
+
+def test_rotate_kernel_choice():
+    """Which rotate+quant kernel each width gets (no GPU needed)."""
+    fast28 = {3584, 7168, 14336}
+    for n in (2, 28, 56, 1792, 3584, 7168, 14336, 28672, 2048, 4096, 8192, 16384, 32768):
+        name = R.kernel_name(n)
+        if n == 28672:
+            assert name == "rq_mfma56_w14"
+        elif n in fast28:
+            assert name == "rq_mfma28_w7"
+        elif n in (4096, 8192, 16384):
+            assert name == "rq_mfma32_w8"
+        else:
+            assert name == "rq_generic", (n, name)
+    assert R.kernel_name(6) is None

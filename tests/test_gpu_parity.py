@@ -191,7 +191,7 @@ def test_no_outlier_control_batch():
 # --------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("n", [4096, 8192, 14336, 28672, 28, 2])
+@pytest.mark.parametrize("n", [4096, 8192, 16384, 3584, 7168, 14336, 28672, 28, 2])
 def test_degenerate_rows(n):
     c = n // 3
     rows = np.zeros((6, n), np.uint16)
@@ -209,7 +209,9 @@ def test_degenerate_rows(n):
 
 
 @pytest.mark.parametrize("n,counts", [(14336, (1, 3, 255, 257, 1031)), (4096, (1, 5, 511, 513, 1537)),
-                                      (8192, (1, 7, 511, 513, 1031)), (28672, (1, 3, 255, 257, 521))])
+                                      (8192, (1, 7, 511, 513, 1031)), (28672, (1, 3, 255, 257, 521)),
+                                      (16384, (1, 3, 255, 513)), (3584, (1, 9, 1023, 1025, 2053)),
+                                      (7168, (1, 5, 511, 513, 1031))])
 def test_strided_rows_and_ragged_token_counts(n, counts):
     """Row stride ld = n + 64 and token counts around the launch grid (one
     or several rows per workgroup, fewer rows than workgroups); rows are
