@@ -144,7 +144,7 @@ def bench_fold(args, torch, R, W) -> int:
     ms = e0.elapsed_time(e1) / args.steps
     bpr = 2 * n + 4 * n  # bf16 row in, fp32 row out
     achieved = bpr * rows / (ms * 1e-3) / 1e9
-    print(json.dumps({
+    line = {
         "metric": "weight rows/s and achieved HBM GB/s, SignRot offline weight fold W' = W.H.D/sqrt(n)",
         "value": rows * args.steps / wall, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
@@ -156,8 +156,39 @@ def bench_fold(args, torch, R, W) -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_row": bpr,
                      "kernel_avg_ms": ms},
-    }), flush=True)
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_fold(w, d)
+    print(json.dumps(line), flush=True)
     return 0
+
+
+def cpu_baseline_fold(w, d, budget_s: float = 12.0) -> dict:
+    """The oracle's fold_weights (float64 dense rotation) on 64-row chunks of
+    the same W, for about budget_s seconds."""
+    import torch
+
+    import oracle as O
+
+    wb = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    dn = d.cpu().numpy()
+    chunk, done = 64, 0
+    t0 = time.perf_counter()
+    while done + chunk <= wb.shape[0]:
+        O.fold_weights(wb[done:done + chunk], dn)
+        done += chunk
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    return {"value": done / dt, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} rows of the same W (n={wb.shape[1]}), oracle fold_weights (float64 dense "
+                      f"rotation), {dt:.1f} s"}
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -445,6 +476,17 @@ def main() -> int:
     ev3.record(stream)
     torch.cuda.synchronize()
     dvec_ms = ev2.elapsed_time(ev3) / dsteps
+    # and through the integer zero-point variant
+    ev2.record(stream)
+    for i in range(dsteps):
+        co, sc, ze = outs[i % nsets]
+        st = L.signrot_rotate_quant_int4_zint(xs[i % nsets].data_ptr(), t, n, n, c, sigma, co.data_ptr(),
+                                             sc.data_ptr(), ze.data_ptr(), sptr)
+        if st != 0:
+            R.check(st, "signrot_rotate_quant_int4_zint")
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    zint_ms = ev2.elapsed_time(ev3) / dsteps
 
     if args.pmc_copy:
         # plain copies of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
@@ -483,6 +525,7 @@ def main() -> int:
             "kernel": kname,
             "entry_point": "signrot_rotate_quant_int4_outlier (d = sigma * row c of H, from calibration)",
             "d_vector_entry_point_kernel_avg_ms": dvec_ms,
+            "integer_zero_point_variant_kernel_avg_ms": zint_ms,
             "input_buffer_sets": nsets,
             "hbm_gbs_wall": bpt * tokens_per_s / 1e9,
             "pct_of_peak_hbm_wall": 100.0 * bpt * tokens_per_s / 1e9 / PEAK_HBM_GBS,

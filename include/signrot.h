@@ -140,6 +140,25 @@ int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_
                                       void* stream);
 
 /*
+ * A variant with an integer zero-point (the GyRot abstract, on the pages as a
+ * related paper: asymmetric quantization reformulated with a rounded
+ * zero-point so that dequantization is integer arithmetic times one scale).
+ * With the same scale s = (mx - mn) / 15 (1 when mx == mn):
+ *   zero = rint(-mn / s), an integer (stored exactly in the float output);
+ *   q_j  = clamp(rint(y_j / s) + zero, 0, 15),
+ * so y_hat = s * (q - zero) with (q - zero) an integer.  Rounding the
+ * zero-point moves the window of 16 levels by at most half a step, so
+ * y / s + zero stays in [-0.5, 15.5] and every value is still within s/2 of
+ * its level.
+ *
+ * The sign vector is given as (c, sigma) as for
+ * signrot_rotate_quant_int4_outlier; there is no y_out.  Same arguments,
+ * alignment and errors as that call.  Asynchronous.
+ */
+int signrot_rotate_quant_int4_zint(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c, int sigma,
+                                   uint8_t* codes, float* scale, float* zero, void* stream);
+
+/*
  * Dequantization: y_hat[t][j] = scale[t] * (q_j - zero[t]), the level value
  * of each code (mn + q * scale).  codes/scale/zero as produced above; y_hat
  * device [tokens][n] float.  n must be supported.  Asynchronous.

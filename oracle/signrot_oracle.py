@@ -282,6 +282,24 @@ def quant_asym(y: np.ndarray, precision: str = "f64"):
     return q, s.astype(np.float64), z.astype(np.float64)
 
 
+def quant_asym_zint(y: np.ndarray, precision: str = "f64"):
+    """Per-token asymmetric INT4 with an integer zero-point (the GyRot
+    abstract, a related paper on the pages: the zero-point is rounded so that
+    dequantization is integer arithmetic times the scale; READING of the
+    formula, which the abstract does not print): s as in quant_asym,
+    z = round_half_even(-mn / s), q = clip(round_half_even(y / s) + z, 0, 15).
+    Returns (codes uint8 [T, n], scale [T], zero [T]) with integral zero."""
+    dt = {"f64": np.float64, "f32": np.float32}[precision]
+    yy = np.asarray(y).astype(dt)
+    mn = yy.min(axis=1)
+    mx = yy.max(axis=1)
+    s = (mx - mn) / dt(15)
+    s = np.where(s == 0, dt(1), s).astype(dt)
+    z = np.rint(-mn / s).astype(dt)
+    q = np.clip(np.rint(yy / s[:, None]) + z[:, None], 0, 15).astype(np.uint8)
+    return q, s.astype(np.float64), z.astype(np.float64)
+
+
 def code_position(y: np.ndarray, precision: str = "f64") -> np.ndarray:
     """(y - mn)/s per element, before rounding (used to find elements that sit
     next to a rounding boundary)."""

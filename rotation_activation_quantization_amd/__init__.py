@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_rotate_quant_int4.restype = ctypes.c_int
     L.signrot_rotate_quant_int4_outlier.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     L.signrot_rotate_quant_int4_outlier.restype = ctypes.c_int
+    L.signrot_rotate_quant_int4_zint.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
+    L.signrot_rotate_quant_int4_zint.restype = ctypes.c_int
     L.signrot_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
     L.signrot_dequant.restype = ctypes.c_int
     L.signrot_fold_weights.argtypes = [vp, i64, i64, i64, vp, vp, vp]
@@ -76,6 +78,7 @@ EXPORTED = (
     "signrot_calibrate",
     "signrot_rotate_quant_int4",
     "signrot_rotate_quant_int4_outlier",
+    "signrot_rotate_quant_int4_zint",
     "signrot_dequant",
     "signrot_fold_weights",
     "signrot_weight_rowsum",
@@ -186,6 +189,24 @@ def signrot_rotate_quant_int4_outlier(x, c: int, sigma: int, y_out: bool = False
     return (codes, scale, zero, y) if y is not None else (codes, scale, zero)
 
 
+def signrot_rotate_quant_int4_zint(x, c: int, sigma: int, out=None):
+    """The integer zero-point variant: zero = rint(-mn / s) (integral floats),
+    codes = clamp(rint(y / s) + zero, 0, 15); d given as (c, sigma)."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    if out is None:
+        codes = torch.empty((t, n // 2), dtype=torch.uint8, device=x.device)
+        scale = torch.empty(t, dtype=torch.float32, device=x.device)
+        zero = torch.empty(t, dtype=torch.float32, device=x.device)
+    else:
+        codes, scale, zero = out[:3]
+    check(lib().signrot_rotate_quant_int4_zint(ptr, t, n, ld, int(c), int(sigma), codes.data_ptr(),
+                                               scale.data_ptr(), zero.data_ptr(), _stream_of(x)),
+          "signrot_rotate_quant_int4_zint")
+    return codes, scale, zero
+
+
 def signrot_dequant(codes, scale, zero, n: int | None = None):
     """codes u8 [T, n/2], scale/zero f32 [T] -> y_hat f32 [T, n]."""
     import torch
@@ -262,6 +283,7 @@ def int4_linear_kernel_name(codes, w) -> str | None:
 calibrate = signrot_calibrate
 rotate_quant_int4 = signrot_rotate_quant_int4
 rotate_quant_int4_outlier = signrot_rotate_quant_int4_outlier
+rotate_quant_int4_zint = signrot_rotate_quant_int4_zint
 dequant = signrot_dequant
 fold_weights = signrot_fold_weights
 weight_rowsum = signrot_weight_rowsum

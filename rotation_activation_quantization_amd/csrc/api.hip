@@ -183,9 +183,11 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   return SIGNROT_OK;
 }
 
-int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c,
-                                      int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
-                                      void* stream) {
+}  // extern "C"
+
+namespace {
+int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c, int sigma,
+                              uint8_t* codes, float* scale, float* zero, float* y_out, int zint, void* stream) {
   g_last_error[0] = '\0';
   const Shape sh = factor_n(n);
   if (!sh.ok) {
@@ -220,6 +222,7 @@ int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_
   a.form_given = 1;
   a.form_c = static_cast<int>(c);
   a.form_neg = sigma < 0 ? 1 : 0;
+  a.zint = zint;
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (rq_fast_supports(sh.n, sh.k, sh.m28)) {
@@ -241,6 +244,20 @@ int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4_outlier launch");
   return SIGNROT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c,
+                                      int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
+                                      void* stream) {
+  return rotate_quant_outlier_impl(x_bf16, tokens, n, ld, c, sigma, codes, scale, zero, y_out, 0, stream);
+}
+
+int signrot_rotate_quant_int4_zint(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c, int sigma,
+                                   uint8_t* codes, float* scale, float* zero, void* stream) {
+  return rotate_quant_outlier_impl(x_bf16, tokens, n, ld, c, sigma, codes, scale, zero, nullptr, 1, stream);
 }
 
 int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,

@@ -47,6 +47,7 @@ struct RqArgs {
   int form_given;      // 1: d = sigma * (row form_c of H) is given by (form_c, form_neg); d unused
   int form_c;
   int form_neg;        // 1 when sigma = -1
+  int zint;            // 1: integer zero-point z = rint(-mn / s), q = clamp(rint(y / s) + z, 0, 15)
   uint32_t h28mask[28];
 };
 

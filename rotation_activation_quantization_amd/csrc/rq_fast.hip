@@ -83,7 +83,7 @@ __device__ __forceinline__ uint32_t quad_slot(uint32_t q) {
   return 16u * u + ((q >> S::LG) ^ (u * S::SWZ));
 }
 
-template <int KA, int KB, bool GENERAL, bool YOUT>
+template <int KA, int KB, bool GENERAL, bool YOUT, bool ZINT = false>
 __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbits, const uint32_t* h28,
                              const DForm& form, float* red, float* xcl) {
   using S = FastShape<KA, KB>;
@@ -360,10 +360,18 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     // (5) quantize, pack, store
     const QuantParams qp = quant_params(mn, mx);
     const float shift = GENERAL ? 0.0f : (sig > 0 ? xcl[par] : -xcl[par]);
+    // code of value v: rne(v * inv + cq); with the integer zero-point z the
+    // code is rne((v + shift) * inv + z), so cq = shift * inv + z
+    float cq = qp.cq;
+    float zq = 0.0f;
+    if constexpr (ZINT) {
+      zq = qp.degenerate ? rintf(-((mn + shift) * a.inv_sqrt_n)) : rintf(-(mn + shift) * qp.inv);
+      cq = qp.degenerate ? 0.0f : fmaf(shift, qp.inv, zq);
+    }
     if (tid == 0) {
       a.scale[row] = qp.degenerate ? 1.0f : qp.range * a.inv_15sqrt_n;
       // zero = -(mn / sqrt(n)) / s with s = range / (15 sqrt(n)) = -(mn + shift) * inv
-      a.zero[row] = qp.degenerate ? -((mn + shift) * a.inv_sqrt_n) : -(mn + shift) * qp.inv;
+      a.zero[row] = ZINT ? zq : (qp.degenerate ? -((mn + shift) * a.inv_sqrt_n) : -(mn + shift) * qp.inv);
     }
     uint32_t q[NT / 2];
 #pragma unroll
@@ -371,8 +379,15 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       uint32_t ev = 0u, od = 0u;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        ev = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[8 * u + 2 * k], qp.inv, qp.cq), k, ev);
-        od = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(v[8 * u + 2 * k + 1], qp.inv, qp.cq), k, od);
+        float fe = fmaf(v[8 * u + 2 * k], qp.inv, cq);
+        float fo = fmaf(v[8 * u + 2 * k + 1], qp.inv, cq);
+        if constexpr (ZINT) {
+          // the rounded zero-point can put the top of the range at 15.5
+          fe = fminf(fe, 15.0f);
+          fo = fminf(fo, 15.0f);
+        }
+        ev = __builtin_amdgcn_cvt_pk_u8_f32(fe, k, ev);
+        od = __builtin_amdgcn_cvt_pk_u8_f32(fo, k, od);
       }
       q[u] = ev | (od << 4);
     }
@@ -403,7 +418,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   wait_vmcnt<0>();
 }
 
-template <int KA, int KB, bool YOUT>
+template <int KA, int KB, bool YOUT, bool ZINT = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void rq_fast_kernel(RqArgs a) {
   using S = FastShape<KA, KB>;
@@ -433,8 +448,13 @@ void rq_fast_kernel(RqArgs a) {
     __syncthreads();
     form = decode_d_form_fast(a, dbits, h28_lds, scratch);
   }
-  if (form.structured) rq_fast_body<KA, KB, false, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
-  else rq_fast_body<KA, KB, true, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
+  if constexpr (ZINT) {
+    // only with d given as (c, sigma): always the structured form
+    rq_fast_body<KA, KB, false, YOUT, true>(a, lds, dbits, h28_lds, form, red, xcl);
+  } else {
+    if (form.structured) rq_fast_body<KA, KB, false, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
+    else rq_fast_body<KA, KB, true, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
+  }
 }
 
 template <int KA, int KB>
@@ -454,7 +474,9 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
   if (grid > a.tokens) grid = a.tokens;
   const dim3 blocks(static_cast<unsigned>(grid));
   const dim3 threads(static_cast<unsigned>(S::kThreads));
-  if (a.yout)
+  if (a.zint)
+    rq_fast_kernel<KA, KB, false, true><<<blocks, threads, 0, stream>>>(a);  // no y_out with zint
+  else if (a.yout)
     rq_fast_kernel<KA, KB, true><<<blocks, threads, 0, stream>>>(a);
   else
     rq_fast_kernel<KA, KB, false><<<blocks, threads, 0, stream>>>(a);

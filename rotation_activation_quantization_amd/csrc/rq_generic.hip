@@ -136,22 +136,33 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(RqArgs a) {
     const bool degenerate = !(range > 0.0f);
     const float inv = degenerate ? 0.0f : 15.0f / range;
 
-    uint8_t* crow = a.codes + t * (n / 2);
-    for (int m = tid; m < n / 2; m += nt) {
-      const float q0 = fminf(fmaxf(rintf((row[2 * m] - mn) * inv), 0.0f), 15.0f);
-      const float q1 = fminf(fmaxf(rintf((row[2 * m + 1] - mn) * inv), 0.0f), 15.0f);
-      crow[m] = static_cast<uint8_t>(static_cast<uint32_t>(q0) | (static_cast<uint32_t>(q1) << 4));
-    }
     const float shift = form.neg ? -xc : xc;
+    const float s = degenerate ? 1.0f : range * a.inv_15sqrt_n;
+    const float mn_y = (mn + shift) * a.inv_sqrt_n;
+    // integer zero-point: z = rint(-mn_y / s), code = clamp(rint((u + shift) * inv + z), 0, 15)
+    const float zq = rintf(-mn_y / s);
+    uint8_t* crow = a.codes + t * (n / 2);
+    if (a.zint) {
+      const float off = degenerate ? 0.0f : fmaf(shift, inv, zq);
+      for (int m = tid; m < n / 2; m += nt) {
+        const float q0 = fminf(fmaxf(rintf(fmaf(row[2 * m], inv, off)), 0.0f), 15.0f);
+        const float q1 = fminf(fmaxf(rintf(fmaf(row[2 * m + 1], inv, off)), 0.0f), 15.0f);
+        crow[m] = static_cast<uint8_t>(static_cast<uint32_t>(q0) | (static_cast<uint32_t>(q1) << 4));
+      }
+    } else {
+      for (int m = tid; m < n / 2; m += nt) {
+        const float q0 = fminf(fmaxf(rintf((row[2 * m] - mn) * inv), 0.0f), 15.0f);
+        const float q1 = fminf(fmaxf(rintf((row[2 * m + 1] - mn) * inv), 0.0f), 15.0f);
+        crow[m] = static_cast<uint8_t>(static_cast<uint32_t>(q0) | (static_cast<uint32_t>(q1) << 4));
+      }
+    }
     if (a.yout) {
       float* yr = a.yout + t * n;
       for (int j = tid; j < n; j += nt) yr[j] = (row[j] + shift) * a.inv_sqrt_n;
     }
     if (tid == 0) {
-      const float s = degenerate ? 1.0f : range * a.inv_15sqrt_n;
-      const float mn_y = (mn + shift) * a.inv_sqrt_n;
       a.scale[t] = s;
-      a.zero[t] = -mn_y / s;
+      a.zero[t] = a.zint ? zq : -mn_y / s;
     }
     __syncthreads();
   }

@@ -208,3 +208,16 @@ def test_rotate_kernel_choice():
         else:
             assert name == "rq_generic", (n, name)
     assert R.kernel_name(6) is None
+
+
+def test_rotate_quant_zint_argument_errors(L):
+    def rq(x=FAKE, t=4, n=4096, ld=4096, c=5, sigma=1, codes=FAKE, scale=FAKE, zero=FAKE):
+        return L.signrot_rotate_quant_int4_zint(x, t, n, ld, c, sigma, codes, scale, zero, None)
+
+    assert rq(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert rq(c=-1) == R.SIGNROT_EINVAL
+    assert rq(c=4096) == R.SIGNROT_EINVAL
+    assert rq(sigma=0) == R.SIGNROT_EINVAL
+    assert rq(ld=4095) == R.SIGNROT_EINVAL
+    assert rq(scale=None) == R.SIGNROT_EINVAL
+    assert rq(t=0, x=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK

@@ -1,0 +1,111 @@
+"""The integer zero-point variant signrot_rotate_quant_int4_zint against the
+oracle's quant_asym_zint.
+
+Decisions taken in binary32 on both sides can part only next to a rounding
+boundary: the zero-point z = rint(-mn/s) may differ by one where -mn/s lies
+within 1e-4 of a half-integer, and a code may differ by one where y/s lies
+within 1e-4 of one (at most 1e-4 of the elements).  Codes are compared as
+levels m = q - z, which a shifted zero-point leaves unchanged except where one
+side clamps.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import rotation_activation_quantization_amd as R  # noqa: E402
+import signrot_workloads as W  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+BOUNDARY = 1e-4
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits):
+    t, n = bits.shape
+    ld = (n + 7) // 8 * 8
+    buf = np.zeros((max(t, 1), ld), np.uint16)
+    buf[:t, :n] = bits
+    return torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)[:t, :n]
+
+
+def near_half(p):
+    return np.abs(p - np.floor(p) - 0.5) < BOUNDARY
+
+
+def compare_zint(y, codes, scale, zero, label):
+    q32, _, z32 = O.quant_asym_zint(y, "f32")
+    _, s64, _ = O.quant_asym_zint(y, "f64")
+    assert np.all(np.abs(scale - s64) <= 1e-6 * s64), label
+    assert np.all(zero == np.rint(zero)), label
+    mn = y.min(axis=1)
+    zpos = -mn / s64
+    dz = zero - z32
+    assert np.all((dz == 0) | (near_half(zpos) & (np.abs(dz) == 1))), label
+    q = O.unpack_int4(codes).astype(np.int64)
+    m_gpu = q - zero[:, None].astype(np.int64)
+    m_ora = q32.astype(np.int64) - z32[:, None].astype(np.int64)
+    diff = m_gpu != m_ora
+    pos = y / s64[:, None]
+    at_boundary = near_half(pos)
+    clamped = (q == 0) | (q == 15) | (q32 == 0) | (q32 == 15)
+    allowed = (at_boundary & (np.abs(m_gpu - m_ora) <= 1)) | ((dz != 0)[:, None] & clamped)
+    assert np.all(~diff | allowed), label
+    assert int((diff & at_boundary).sum()) <= math.ceil(BOUNDARY * y.size), label
+    return int(diff.sum()), int((dz != 0).sum())
+
+
+@pytest.mark.parametrize("n,t", [(4096, 64), (8192, 40), (14336, 48), (28672, 12), (3584, 40), (16384, 10),
+                                 (28, 9), (1792, 17)])
+def test_zint_matches_oracle(n, t):
+    g = np.random.default_rng([83, n])
+    for c, sigma in ((int(g.integers(n)), 1), (int(g.integers(n)), -1)):
+        bits = W.random_rows(t, n, seed=c, scale=0.7, outlier=1300.0 * sigma)
+        bits[::4, c] = W.f32_to_bf16_bits(np.array([0.3], np.float32))[0]  # some rows without the outlier
+        d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+        say(f"[gpu] zint n={n} T={t} c={c} sigma={sigma} kernel={R.kernel_name(n)}")
+        codes, scale, zero = R.rotate_quant_int4_zint(dev(bits), c, sigma)
+        torch.cuda.synchronize()
+        y = O.rotate(O.bf16_bits_to_f64(bits), d)
+        st = compare_zint(y, codes.cpu().numpy(), scale.cpu().numpy(), zero.cpu().numpy(), f"zint n={n}")
+        say(f"[gpu] zint n={n}: level mismatches {st[0]}, zero-point differences {st[1]}")
+
+
+@pytest.mark.parametrize("n", [14336, 4096, 28])
+def test_zint_degenerate_rows(n):
+    c = n // 3
+    rows = np.zeros((4, n), np.uint16)
+    rows[1, :] = W.f32_to_bf16_bits(np.full(n, 2.5, np.float32))
+    rows[2, c] = W.f32_to_bf16_bits(np.array([1512.0], np.float32))[0]
+    rows[3] = W.random_rows(1, n, seed=3, scale=1e-3)[0]
+    d = O.calibrate(rows[2:3])["d"]
+    ref = O.calibrate(rows[2:3])
+    codes, scale, zero = R.rotate_quant_int4_zint(dev(rows), ref["c"], ref["sigma"])
+    torch.cuda.synchronize()
+    y = O.rotate(O.bf16_bits_to_f64(rows), d)
+    compare_zint(y, codes.cpu().numpy(), scale.cpu().numpy(), zero.cpu().numpy(), f"zint degenerate n={n}")
+    assert scale[0].item() == 1.0 and np.all(codes[0].cpu().numpy() == 0)
+
+
+def test_zint_workload_levels_dequantize_within_half_a_step():
+    """On the n = 14336 workload: every dequantized value s * (q - z) is within
+    s/2 of the oracle's rotated value (plus binary32 slack)."""
+    cal, _ = W.calibration_batch("target")
+    bits, _ = W.batch("target", tokens=256)
+    ref = O.calibrate(cal)
+    codes, scale, zero = R.rotate_quant_int4_zint(dev(bits), ref["c"], ref["sigma"])
+    torch.cuda.synchronize()
+    y = O.rotate(O.bf16_bits_to_f64(bits), ref["d"])
+    q = O.unpack_int4(codes.cpu().numpy()).astype(np.float64)
+    s = scale.cpu().numpy().astype(np.float64)[:, None]
+    yhat = s * (q - zero.cpu().numpy().astype(np.float64)[:, None])
+    assert np.all(np.abs(yhat - y) <= s / 2 * (1 + 1e-4) + 1e-5 * np.abs(y).max(axis=1, keepdims=True))

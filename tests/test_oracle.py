@@ -609,3 +609,53 @@ def test_quantized_product_on_the_folded_weight_approximates_the_projection(n):
     assert np.all(np.abs(got - ref) <= bound * (1 + 1e-9) + 1e-12)
     # and the bound is not vacuous: the product keeps most of the signal
     assert np.linalg.norm(got - ref) < 0.2 * np.linalg.norm(ref)
+
+
+# ---------------------------------------------------------------------------
+# Integer zero-point variant (the GyRot abstract on the pages: a rounded
+# zero-point that makes dequantization integer arithmetic)
+# ---------------------------------------------------------------------------
+
+
+def test_zint_codes_are_the_nearest_level_of_the_integer_window():
+    """Brute force: with the window of levels s*(k - z), k = 0..15, each code
+    is the index of the nearest level (ties to the even k), and z is the
+    integer nearest to -mn/s."""
+    g = np.random.default_rng(81)
+    y = np.concatenate([g.normal(0, 1, (6, 20)), 14 + g.random((3, 20)) * 2.5, -30 + g.random((2, 20))])
+    q, s, z = O.quant_asym_zint(y, "f64")
+    for t in range(y.shape[0]):
+        mn = y[t].min()
+        assert z[t] == float(round(-mn / s[t]))
+        for j in range(y.shape[1]):
+            dist = [abs(y[t, j] - s[t] * (k - z[t])) for k in range(16)]
+            best = min(range(16), key=lambda k: (dist[k], k % 2))
+            assert q[t, j] == best
+
+
+def test_zint_error_bound_and_integer_dequant():
+    """Every value is within s/2 of its level (the rounded zero-point moves the
+    window by at most half a step), and q - z is an integer."""
+    g = np.random.default_rng(82)
+    y = np.concatenate([g.normal(0, 3, (20, 256)), 12 + g.random((20, 256)) * 4])
+    q, s, z = O.quant_asym_zint(y, "f64")
+    yhat = s[:, None] * (q.astype(np.float64) - z[:, None])
+    assert np.all(np.abs(yhat - y) <= s[:, None] / 2 * (1 + 1e-12))
+    assert np.all(z == np.rint(z))
+
+
+def test_zint_equals_the_float_zero_point_quantizer_when_the_zero_is_integral():
+    """When -mn/s is already an integer the two quantizers coincide."""
+    s = 0.25
+    y = np.array([[-2.0, -1.9, 0.1, 0.37, 1.0, 1.75]])
+    y[0, -1] = y[0, 0] + 15 * s  # range exactly 15 steps, -mn/s = 8
+    qz, sz, zz = O.quant_asym_zint(y, "f64")
+    qf, sf, zf = O.quant_asym(y, "f64")
+    assert sz[0] == sf[0] == s and zz[0] == zf[0] == 8.0
+    assert np.array_equal(qz, qf)
+
+
+def test_zint_degenerate_row():
+    y = np.full((1, 8), 2.3)
+    q, s, z = O.quant_asym_zint(y, "f64")
+    assert s[0] == 1.0 and z[0] == -2.0 and np.all(q == 0)
