@@ -221,3 +221,19 @@ def test_rotate_quant_zint_argument_errors(L):
     assert rq(ld=4095) == R.SIGNROT_EINVAL
     assert rq(scale=None) == R.SIGNROT_EINVAL
     assert rq(t=0, x=None, codes=None, scale=None, zero=None) == R.SIGNROT_OK
+
+
+def test_header_is_plain_c(tmp_path):
+    """include/signrot.h compiles as C99 on its own (no C++ or HIP types leak
+    into the boundary), and its prototypes match a C caller."""
+    src = tmp_path / "use_header.c"
+    src.write_text(
+        '#include "signrot.h"\n'
+        "int probe(void) {\n"
+        "  int (*f)(const void*, int64_t, int64_t, int64_t, int64_t, int, uint8_t*, float*, float*, float*,\n"
+        "           void*) = signrot_rotate_quant_int4_outlier;\n"
+        "  return f != 0 && signrot_supported_n(14336) == 1;\n"
+        "}\n")
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
+                        "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
