@@ -38,7 +38,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 PEAK_HBM_GBS = 8000.0  # MI355X published HBM3E bandwidth
-WORKLOAD = "target"
+WORKLOAD = "n14336_t8192"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # Sources that define the timed kernel; the HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
@@ -119,7 +119,7 @@ def bench_fold(args, torch, R, W) -> int:
     rows, n = 4096, 14336
     g = torch.Generator(device="cpu").manual_seed(2611)
     w = (torch.randn((rows, n), generator=g) / n ** 0.5).to(torch.bfloat16).cuda()
-    d = R.calibrate(to_dev_bits(W.calibration_batch("target")[0], torch))[0]
+    d = R.calibrate(to_dev_bits(W.calibration_batch("n14336_t8192")[0], torch))[0]
     out = torch.empty((rows, n), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     fn = R.lib().signrot_fold_weights
@@ -201,9 +201,9 @@ def bench_linear(args, torch, R, W) -> int:
     (synthetic N(0, 1/n), folded with the same d).  One step = one
     signrot_int4_linear call over the whole batch."""
     rows = 4096
-    bits, _ = W.batch("target")
+    bits, _ = W.batch("n14336_t8192")
     t, n = bits.shape
-    d = R.calibrate(to_dev_bits(W.calibration_batch("target")[0], torch))[0]
+    d = R.calibrate(to_dev_bits(W.calibration_batch("n14336_t8192")[0], torch))[0]
     codes, scale, zero = R.rotate_quant_int4(to_dev_bits(bits, torch), d)
     g = torch.Generator(device="cpu").manual_seed(2612)
     w = (torch.randn((rows, n), generator=g) / n ** 0.5).to(torch.bfloat16).cuda()
@@ -323,7 +323,7 @@ def decode_latency(R, W, torch, c, sigma, calls: int = 10000) -> dict:
     out = {}
     fn = R.lib().signrot_rotate_quant_int4_outlier
     for t in (1, 4, 16):
-        bits, _ = W.decode_batch("cfg5", t, 0)
+        bits, _ = W.decode_batch("n14336_decode", t, 0)
         n = bits.shape[1]
         x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
         co = torch.empty((t, n // 2), dtype=torch.uint8, device="cuda")
@@ -389,7 +389,7 @@ def main() -> int:
     ap.add_argument("--linear", action="store_true",
                     help="time the INT4-activation down-projection signrot_int4_linear instead "
                          "(8192 x 14336 codes, W' 4096 x 14336 bf16)")
-    ap.add_argument("--workload", default=WORKLOAD, choices=["cfg1", "cfg2", "cfg3", "target", "cfg4"],
+    ap.add_argument("--workload", default=WORKLOAD, choices=["n4096_t64", "n8192_t2048", "n14336_t4096", "n14336_t8192", "n28672_t8192"],
                     help="synthetic workload to time (default: n=14336 x 8192 tokens)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -10,7 +10,7 @@ of the MLP hidden layer): Gaussian or Student-t background activations, one
 and, for the widest case, a few mildly amplified channels.  Values are drawn
 in float32 and rounded to bf16 (round to nearest, ties to even).
 
-Random streams: numpy.random.default_rng([2611, cfg, stream]) with
+Random streams: numpy.random.default_rng([2611, seed, stream]) with
 stream 0 = the batch, 1 = the calibration batch, 2 = channel choices,
 3 = the no-outlier control batch, 100 + r = decode repetition r.
 """
@@ -28,7 +28,7 @@ _CHUNK = 256  # rows drawn per call: fixes the draw order, bounds memory
 @dataclass(frozen=True)
 class Workload:
     name: str
-    cfg: int
+    seed: int  # the workload's own seed stream
     n: int
     tokens: int
     law: str  # "normal" or "t"
@@ -48,28 +48,28 @@ class Workload:
 
 WORKLOADS = {
     # n = 2^12, N(0,1), channel 1234 = +M in 25% of tokens, calibrate on the batch
-    "cfg1": Workload("cfg1", 1, 4096, 64, "normal", 1.0, p_outlier=0.25, m_lo=500, m_hi=2000,
+    "n4096_t64": Workload("n4096_t64", 1, 4096, 64, "normal", 1.0, p_outlier=0.25, m_lo=500, m_hi=2000,
                      fixed_channel=1234, calib_tokens=64, calib_same=True),
     # n = 2^13, Student-t(4)*0.5, seeded channel = +-M (90% +) in 30% of tokens
-    "cfg2": Workload("cfg2", 2, 8192, 2048, "t", 0.5, df=4, p_outlier=0.30, m_lo=500, m_hi=2000,
+    "n8192_t2048": Workload("n8192_t2048", 2, 8192, 2048, "t", 0.5, df=4, p_outlier=0.30, m_lo=500, m_hi=2000,
                      p_positive=0.9, calib_tokens=256),
     # n = 28 * 2^9 (LLaMA3-8B down_proj input), N(0, 0.7), +M in 20% of tokens
-    "cfg3": Workload("cfg3", 3, 14336, 4096, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
+    "n14336_t4096": Workload("n14336_t4096", 3, 14336, 4096, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
                      calib_tokens=256),
-    # the throughput workload: cfg3's law at 8192 tokens
-    "target": Workload("target", 3, 14336, 8192, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
+    # the throughput workload: the same law at 8192 tokens
+    "n14336_t8192": Workload("n14336_t8192", 3, 14336, 8192, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
                        calib_tokens=256),
     # n = 28 * 2^10 (LLaMA3-70B), Student-t(3)*0.4, +M in 15%, 8 mild channels x20
-    "cfg4": Workload("cfg4", 4, 28672, 8192, "t", 0.4, df=3, p_outlier=0.15, m_lo=1000, m_hi=3000,
+    "n28672_t8192": Workload("n28672_t8192", 4, 28672, 8192, "t", 0.4, df=3, p_outlier=0.15, m_lo=1000, m_hi=3000,
                      mild_channels=8, mild_factor=20.0, calib_tokens=512),
-    # decode-shaped batches with cfg3's law (1, 4 or 16 tokens per call)
-    "cfg5": Workload("cfg5", 5, 14336, 16, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
+    # decode-shaped batches with the n = 14336 law (1, 4 or 16 tokens per call)
+    "n14336_decode": Workload("n14336_decode", 5, 14336, 16, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
                      calib_tokens=256, extra={"batches": (1, 4, 16), "repeats": 10000}),
 }
 
 
-def rng(cfg: int, stream: int) -> np.random.Generator:
-    return np.random.default_rng([SEED_ROOT, cfg, stream])
+def rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng([SEED_ROOT, seed, stream])
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -81,7 +81,7 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 def channels(w: Workload):
     """(outlier channel c, array of mild channels) drawn from stream 2."""
-    g = rng(w.cfg, 2)
+    g = rng(w.seed, 2)
     c = int(g.integers(0, w.n)) if w.fixed_channel is None else int(w.fixed_channel)
     mild = np.zeros(0, dtype=np.int64)
     if w.mild_channels:
@@ -118,27 +118,27 @@ def batch(name: str, tokens: int | None = None):
     """The workload's token batch: (bf16 bits uint16 [T, n], metadata)."""
     w = WORKLOADS[name]
     t = w.tokens if tokens is None else int(tokens)
-    return _draw(w, t, rng(w.cfg, 0))
+    return _draw(w, t, rng(w.seed, 0))
 
 
 def calibration_batch(name: str):
-    """The calibration batch (cfg1 calibrates on its own batch)."""
+    """The calibration batch (the 64-token n = 4096 workload calibrates on its own batch)."""
     w = WORKLOADS[name]
     if w.calib_same:
         return batch(name)
-    return _draw(w, w.calib_tokens, rng(w.cfg, 1))
+    return _draw(w, w.calib_tokens, rng(w.seed, 1))
 
 
-def control_batch(name: str = "cfg5", tokens: int = 4096):
+def control_batch(name: str = "n14336_decode", tokens: int = 4096):
     """No-outlier control batch with the workload's background law."""
     w = WORKLOADS[name]
-    return _draw(w, tokens, rng(w.cfg, 3), with_outlier=False)
+    return _draw(w, tokens, rng(w.seed, 3), with_outlier=False)
 
 
 def decode_batch(name: str, tokens: int, repetition: int):
     """One decode-shaped batch of `tokens` rows for repetition r."""
     w = WORKLOADS[name]
-    return _draw(w, tokens, rng(w.cfg, 100 + repetition))
+    return _draw(w, tokens, rng(w.seed, 100 + repetition))
 
 
 def random_rows(tokens: int, n: int, seed: int, scale: float = 1.0, outlier: float = 0.0):

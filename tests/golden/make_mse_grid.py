@@ -27,7 +27,7 @@ import oracle as O  # noqa: E402
 import signrot_workloads as W  # noqa: E402
 
 # tokens per workload: enough outlier tokens for a stable mean, bounded CPU time
-SAMPLE = {"cfg1": 64, "cfg2": 512, "cfg3": 512, "cfg4": 192}
+SAMPLE = {"n4096_t64": 64, "n8192_t2048": 512, "n14336_t4096": 512, "n28672_t8192": 192}
 CONTROL_TOKENS = 256
 
 
@@ -65,11 +65,11 @@ def main() -> None:
         grid["workloads"][name] = {"n": int(bits.shape[1]), "sample_tokens": t,
                                    "outlier": summarise(pt, has), "no_outlier": summarise(pt, ~has)}
         print(name, json.dumps(grid["workloads"][name]), flush=True)
-    bits, _ = W.control_batch("cfg5", tokens=CONTROL_TOKENS)
-    d = O.calibrate(W.calibration_batch("cfg5")[0])["d"]
+    bits, _ = W.control_batch("n14336_decode", tokens=CONTROL_TOKENS)
+    d = O.calibrate(W.calibration_batch("n14336_decode")[0])["d"]
     x = O.bf16_bits_to_f64(bits)
     pt = cells(O.rotate(x), O.rotate(x, d))
-    grid["workloads"]["cfg5_control"] = {"n": int(bits.shape[1]), "sample_tokens": CONTROL_TOKENS,
+    grid["workloads"]["n14336_control"] = {"n": int(bits.shape[1]), "sample_tokens": CONTROL_TOKENS,
                                          "no_outlier": summarise(pt, np.ones(CONTROL_TOKENS, bool))}
     with open(os.path.join(HERE, "mse_grid.json"), "w") as f:
         json.dump(grid, f, indent=1)

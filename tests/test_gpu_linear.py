@@ -173,8 +173,8 @@ def test_quantized_chain_on_the_gpu_approximates_the_projection():
     level is within s/2 of its value; x W^T = y W'^T exactly).  s, y and W'
     are the oracle's; W'_bf16 is the rounded weight the product consumed."""
     n, rows = 14336, 96
-    bits, meta = W.batch("cfg3", tokens=48)
-    cal = W.calibration_batch("cfg3")[0]
+    bits, meta = W.batch("n14336_t4096", tokens=48)
+    cal = W.calibration_batch("n14336_t4096")[0]
     g = np.random.default_rng(94)
     w_bits = W.f32_to_bf16_bits((g.standard_normal((rows, n)) / np.sqrt(n)).astype(np.float32))
     say("[gpu] quantized chain n=14336")

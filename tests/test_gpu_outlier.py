@@ -52,8 +52,8 @@ def test_outlier_form_matches_vector_form_and_oracle(n, t):
 
 def test_outlier_form_on_the_workload_with_calibrated_c_and_sigma():
     """(c, sigma) straight from signrot_calibrate on the n = 14336 workload."""
-    cal, _ = W.calibration_batch("target")
-    bits, _ = W.batch("target", tokens=512)
+    cal, _ = W.calibration_batch("n14336_t8192")
+    bits, _ = W.batch("n14336_t8192", tokens=512)
     d, c, _, m = R.calibrate(dev(cal))
     sigma = -1 if m < 0 else 1
     codes, scale, zero = R.rotate_quant_int4_outlier(dev(bits), c, sigma)

@@ -65,7 +65,7 @@ def random_d(n, seed):
 # --------------------------------------------------------------------------
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3", "cfg4"])
+@pytest.mark.parametrize("name", ["n4096_t64", "n8192_t2048", "n14336_t4096", "n28672_t8192"])
 def test_calibrate_bit_exact(name):
     cal_bits, meta = W.calibration_batch(name)
     say(f"[gpu] calibrate {name} T={cal_bits.shape[0]} n={cal_bits.shape[1]}")
@@ -134,8 +134,8 @@ def _workload(name):
     return _cache[name]
 
 
-@pytest.mark.parametrize("name,sample", [("cfg1", None), ("cfg2", None), ("cfg3", 192),
-                                         ("target", 96), ("cfg4", 40)])
+@pytest.mark.parametrize("name,sample", [("n4096_t64", None), ("n8192_t2048", None), ("n14336_t4096", 192),
+                                         ("n14336_t8192", 96), ("n28672_t8192", 40)])
 def test_workload_parity(name, sample):
     bits, meta, cal = _workload(name)
     t, n = bits.shape
@@ -167,13 +167,13 @@ def test_workload_parity(name, sample):
 
 
 def test_decode_batches():
-    cal = O.calibrate(W.calibration_batch("cfg5")[0])
+    cal = O.calibrate(W.calibration_batch("n14336_decode")[0])
     d = cal["d"]
     for batch, reps in ((1, 100), (4, 25), (16, 8)):
         say(f"[gpu] decode batch={batch} reps={reps}")
         allb, allc, alls, allz, ally = [], [], [], [], []
         for r in range(reps):
-            bits, _ = W.decode_batch("cfg5", batch, r)
+            bits, _ = W.decode_batch("n14336_decode", batch, r)
             codes, scale, zero, y = run(bits, d)
             allb.append(bits); allc.append(codes); alls.append(scale); allz.append(zero); ally.append(y)
         compare(expected(np.concatenate(allb), d), np.concatenate(allc), np.concatenate(alls),
@@ -181,8 +181,8 @@ def test_decode_batches():
 
 
 def test_no_outlier_control_batch():
-    bits, _ = W.control_batch("cfg5", tokens=256)
-    cal = O.calibrate(W.calibration_batch("cfg5")[0])
+    bits, _ = W.control_batch("n14336_decode", tokens=256)
+    cal = O.calibrate(W.calibration_batch("n14336_decode")[0])
     check_rows(bits, cal["d"], "control")
 
 
@@ -239,7 +239,7 @@ def test_zero_tokens_is_noop():
 
 
 def test_dequant_matches_oracle():
-    bits, _ = W.batch("cfg1")
+    bits, _ = W.batch("n4096_t64")
     cal = O.calibrate(bits)
     y = O.rotate(O.bf16_bits_to_f64(bits), cal["d"])
     q, s, z = O.quant_asym(y)
@@ -258,9 +258,9 @@ def test_gpu_round_trip_mse_matches_oracle():
     """End to end on the GPU (rotate + quantize, then dequant) the per-token
     quantization MSE of SignRot + asymmetric INT4 equals the oracle's, and on
     outlier tokens it is far below plain Hadamard + symmetric INT4."""
-    bits, meta = W.batch("cfg3", tokens=64)
-    d_np = O.calibrate(W.calibration_batch("cfg3")[0])["d"]
-    say("[gpu] round-trip MSE cfg3 T=64")
+    bits, meta = W.batch("n14336_t4096", tokens=64)
+    d_np = O.calibrate(W.calibration_batch("n14336_t4096")[0])["d"]
+    say("[gpu] round-trip MSE n=14336 T=64")
     x = to_dev(bits)
     codes, scale, zero = R.rotate_quant_int4(x, torch.from_numpy(d_np).cuda())
     yh = R.dequant(codes, scale, zero)
@@ -303,8 +303,8 @@ def test_fold_and_quantized_activations_reproduce_the_projection():
     (float64) to within the INT4 quantization error, and on outlier tokens
     SignRot + asymmetric INT4 is far closer than plain Hadamard + symmetric."""
     n, rows = 14336, 64
-    bits, meta = W.batch("cfg3", tokens=32)
-    d_np = O.calibrate(W.calibration_batch("cfg3")[0])["d"]
+    bits, meta = W.batch("n14336_t4096", tokens=32)
+    d_np = O.calibrate(W.calibration_batch("n14336_t4096")[0])["d"]
     g = np.random.default_rng([43])
     w_bits = W.f32_to_bf16_bits((g.standard_normal((rows, n)) / np.sqrt(n)).astype(np.float32))
     d = torch.from_numpy(d_np).cuda()

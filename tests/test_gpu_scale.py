@@ -30,12 +30,12 @@ def say(msg):
 
 def test_65536_tokens_at_14336_sampled():
     n, t = 14336, 65536
-    base, _ = W.batch("target")  # 8192 rows of the workload law
+    base, _ = W.batch("n14336_t8192")  # 8192 rows of the workload law
     say(f"[gpu] large batch n={n} T={t}")
     x = torch.from_numpy(base.view(np.int16)).cuda().view(torch.bfloat16).repeat(t // base.shape[0], 1)
     g = np.random.default_rng(17)
     rows = np.unique(np.concatenate([[0, t - 1, t // 2], g.choice(t, 29, replace=False)]))
-    cal, _ = W.calibration_batch("target")
+    cal, _ = W.calibration_batch("n14336_t8192")
     ref = O.calibrate(cal)
     codes, scale, zero = R.rotate_quant_int4_outlier(x, ref["c"], ref["sigma"])
     torch.cuda.synchronize()
@@ -51,8 +51,8 @@ def test_65536_tokens_at_14336_sampled():
 
 def test_concurrent_calls_on_separate_streams():
     n = 14336
-    bits, _ = W.batch("target", tokens=1024)
-    cal, _ = W.calibration_batch("target")
+    bits, _ = W.batch("n14336_t8192", tokens=1024)
+    cal, _ = W.calibration_batch("n14336_t8192")
     ref = O.calibrate(cal)
     x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
     want = R.rotate_quant_int4_outlier(x, ref["c"], ref["sigma"])

@@ -99,8 +99,8 @@ def test_zint_degenerate_rows(n):
 def test_zint_workload_levels_dequantize_within_half_a_step():
     """On the n = 14336 workload: every dequantized value s * (q - z) is within
     s/2 of the oracle's rotated value (plus binary32 slack)."""
-    cal, _ = W.calibration_batch("target")
-    bits, _ = W.batch("target", tokens=256)
+    cal, _ = W.calibration_batch("n14336_t8192")
+    bits, _ = W.batch("n14336_t8192", tokens=256)
     ref = O.calibrate(cal)
     codes, scale, zero = R.rotate_quant_int4_zint(dev(bits), ref["c"], ref["sigma"])
     torch.cuda.synchronize()

@@ -262,7 +262,7 @@ def test_symmetric_quantizer_ignores_the_flip():
     """Symmetric-vs-asymmetric paragraph: flipping signs keeps every absolute
     value, so the symmetric grid (sized by max |y|) is unchanged and the codes
     flip with the values; the error is identical."""
-    bits, _ = W.batch("cfg1")
+    bits, _ = W.batch("n4096_t64")
     cal = O.calibrate(bits)
     x = O.bf16_bits_to_f64(bits)
     y = O.rotate(x)
@@ -332,7 +332,7 @@ def test_pack_unpack_roundtrip_and_nibble_order():
 
 
 def test_f32_and_f64_quantizers_agree_away_from_boundaries():
-    bits, _ = W.batch("cfg1")
+    bits, _ = W.batch("n4096_t64")
     y = O.rotate(O.bf16_bits_to_f64(bits), O.calibrate(bits)["d"])
     q64, s64, z64 = O.quant_asym(y, "f64")
     q32, s32, z32 = O.quant_asym(y, "f32")
@@ -381,7 +381,7 @@ def test_calibration_zero_batch_and_negative_zero():
     assert np.array_equal(r["d"], O.hadamard_row(8, 0))
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3"])
+@pytest.mark.parametrize("name", ["n4096_t64", "n8192_t2048", "n14336_t4096"])
 def test_calibration_recovers_planted_channel(name):
     cal_bits, meta = W.calibration_batch(name)
     r = O.calibrate(cal_bits)
@@ -405,8 +405,8 @@ def test_signrot_collapses_bimodal_tokens():
     """Failure-mode and sign-adjustment paragraphs: a dominating outlier splits a
     plainly rotated token into two crowds with an empty middle; after the flip
     the token is one crowd (one sign, contiguous codes)."""
-    bits, meta = W.batch("cfg3", tokens=64)
-    cal = O.calibrate(W.calibration_batch("cfg3")[0])
+    bits, meta = W.batch("n14336_t4096", tokens=64)
+    cal = O.calibrate(W.calibration_batch("n14336_t4096")[0])
     rows = meta["outlier_tokens"][meta["outlier_tokens"] < 64]
     assert len(rows) >= 5
     x = O.bf16_bits_to_f64(bits[rows])
@@ -423,8 +423,8 @@ def test_signrot_collapses_bimodal_tokens():
 def test_mse_ordering_on_outlier_and_control_tokens():
     """SignRot+asym beats plain+asym and plain+sym on outlier tokens; on tokens
     without an outlier it is no worse in a statistically meaningful way."""
-    bits, meta = W.batch("cfg3", tokens=128)
-    cal = O.calibrate(W.calibration_batch("cfg3")[0])
+    bits, meta = W.batch("n14336_t4096", tokens=128)
+    cal = O.calibrate(W.calibration_batch("n14336_t4096")[0])
     x = O.bf16_bits_to_f64(bits)
     y_plain = O.rotate(x)
     y_sr = O.rotate(x, cal["d"])
@@ -458,7 +458,7 @@ def test_mse_grid_directions():
     outlier tokens SignRot + asymmetric INT4 cuts the error of both plain
     quantizers by more than 10x; without an outlier it matches plain + asym."""
     g = _mse_grid()["workloads"]
-    assert set(g) == {"cfg1", "cfg2", "cfg3", "cfg4", "cfg5_control"}
+    assert set(g) == {"n4096_t64", "n8192_t2048", "n14336_t4096", "n28672_t8192", "n14336_control"}
     for name, w in g.items():
         for part in ("outlier", "no_outlier"):
             if part not in w:
@@ -473,10 +473,10 @@ def test_mse_grid_directions():
 
 
 def test_mse_grid_is_the_oracles():
-    """The stored cfg1 cells are what the oracle computes now."""
-    g = _mse_grid()["workloads"]["cfg1"]
-    bits, meta = W.batch("cfg1")
-    d = O.calibrate(W.calibration_batch("cfg1")[0])["d"]
+    """The stored n = 4096 cells are what the oracle computes now."""
+    g = _mse_grid()["workloads"]["n4096_t64"]
+    bits, meta = W.batch("n4096_t64")
+    d = O.calibrate(W.calibration_batch("n4096_t64")[0])["d"]
     x = O.bf16_bits_to_f64(bits)
     y_sr = O.rotate(x, d)
     q, s, z = O.quant_asym(y_sr)
