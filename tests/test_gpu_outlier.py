@@ -60,3 +60,34 @@ def test_outlier_form_on_the_workload_with_calibrated_c_and_sigma():
     ref = R.rotate_quant_int4(dev(bits), d)
     torch.cuda.synchronize()
     assert torch.equal(codes, ref[0]) and torch.equal(scale, ref[1]) and torch.equal(zero, ref[2])
+
+
+@pytest.mark.parametrize("n,t", [(14336, 1), (14336, 45), (14336, 3000), (7168, 37), (7168, 2100), (3584, 9),
+                                 (3584, 1500)])
+def test_outlier_form_without_y_output(n, t):
+    """The calibrated-form entry without y output for n = 28 * 2^k.  The
+    outlier channel is placed once in each of the seven groups of four a-rows
+    (each staged and zeroed by its own wave), with both signs, at row counts
+    below the grid and at several rows per work-group (so that x_c of the next
+    row is taken while the current one is processed).  Codes, scale and zero
+    equal the vector-form call bit for bit, and sampled rows meet the oracle's
+    tolerances."""
+    g = np.random.default_rng([63, n, t])
+    blk = n // 28  # a-row length
+    rows = np.unique(np.concatenate([[0, t - 1], g.choice(t, min(t, 10), replace=False)]))
+    for wv in range(7):
+        c = int((4 * wv + g.integers(4)) * blk + g.integers(blk))
+        sigma = 1 if wv % 2 == 0 else -1
+        bits = W.random_rows(t, n, seed=c, scale=0.8, outlier=700.0 * sigma)
+        bits[1::3, c] = W.f32_to_bf16_bits(np.array([0.25], np.float32))[0]  # rows without the outlier
+        d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+        say(f"[gpu] outlier form, no y: n={n} T={t} c={c} (wave {wv}) sigma={sigma}")
+        x = dev(bits)
+        a = R.rotate_quant_int4_outlier(x, c, sigma)
+        b = R.rotate_quant_int4(x, torch.from_numpy(d).cuda())
+        torch.cuda.synchronize()
+        a = [v.cpu().numpy() for v in a]
+        b = [v.cpu().numpy() for v in b]
+        for u, v, name in zip(a, b, ("codes", "scale", "zero")):
+            assert np.array_equal(u, v), name
+        compare(expected(bits[rows], d), a[0][rows], a[1][rows], a[2][rows], label=f"outlier no-y n={n} c={c}")
