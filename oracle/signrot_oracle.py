@@ -22,9 +22,10 @@ Sources (pages, cited by title and section):
          asymmetric quantizers, and its "Worked example".
 
 Readings where the pages are silent are labelled READING and are collected in
-the design notes; the construction of the order-28 factor (Paley I over
-GF(27)) is not on the pages at all -- the only thing they fix is that the
-transform is a Hadamard matrix with entries +-1/sqrt(n).
+the design notes; the outer Hadamard factors (Paley's constructions I and II
+over GF(q), order 28 by construction I over GF(27)) are not on the pages at
+all -- the only thing they fix is that the transform is a Hadamard matrix
+with entries +-1/sqrt(n).
 
 Parity status: every public function below is pinned by the oracle self-tests
 (closed forms, the pages' printed numbers, textbook identities, brute force).
@@ -112,29 +113,191 @@ def paley28() -> np.ndarray:
     return (np.eye(28, dtype=np.int64) + s).astype(np.int8)
 
 
+# --- general outer factors (READING: the pages fix no Hadamard order) -------
+#
+# n = o * 2^v with o odd.  o = 1: the Sylvester matrix of order n.  Otherwise
+# H_n = H_m (x) H_{2^k} with m = o * 2^j for the smallest j >= 2 such that a
+# Paley matrix of order m exists and m <= MAX_OUTER (k = v - j), Paley I
+# preferred over Paley II.  Order 28 (o = 7) is the paley28() matrix above.
+# GF(p^e) uses the first monic irreducible polynomial of degree e over GF(p)
+# in lexicographic order of its coefficients (a_{e-1}, ..., a_0), and the
+# element with base-p digits (c_0, c_1, ...) has index c_0 + c_1 p + ...;
+# for GF(27) that is t^3 + 2t + 1, the paley28() modulus.
+
+MAX_OUTER = 512
+
+
+def _is_prime(p: int) -> bool:
+    return p >= 2 and all(p % d for d in range(2, int(math.isqrt(p)) + 1))
+
+
+def prime_power(q: int):
+    """(p, e) with q = p^e, p prime, or None."""
+    for p in range(2, q + 1):
+        if q % p == 0:
+            if not _is_prime(p):
+                return None
+            e = 0
+            while q % p == 0:
+                q //= p
+                e += 1
+            return (p, e) if q == 1 else None
+    return None
+
+
+def _poly_divides(f, g, p):
+    """True when monic g divides f over GF(p) (coefficient lists, low first)."""
+    r = list(f)
+    dg = len(g) - 1
+    for d in range(len(r) - 1, dg - 1, -1):
+        c = r[d] % p
+        if c:
+            for t in range(dg + 1):
+                r[d - dg + t] = (r[d - dg + t] - c * g[t]) % p
+    return all(v % p == 0 for v in r[:dg])
+
+
+def gf_modulus(p: int, e: int):
+    """The first monic irreducible polynomial of degree e over GF(p), as the
+    coefficient list [a_0, ..., a_{e-1}, 1] (lexicographic in a_{e-1} .. a_0)."""
+    import itertools
+
+    def monic(deg):
+        for cs in itertools.product(range(p), repeat=deg):
+            yield list(reversed(cs)) + [1]
+
+    for cs in itertools.product(range(p), repeat=e):
+        f = list(reversed(cs)) + [1]
+        if all(not _poly_divides(f, g, p) for d in range(1, e // 2 + 1) for g in monic(d)):
+            return f
+    raise ValueError("no irreducible polynomial")
+
+
+class GF:
+    """GF(q), q = p^e: elements are indices 0..q-1 (base-p digits are the
+    polynomial coefficients); arithmetic from the definitions."""
+
+    def __init__(self, q: int):
+        pe = prime_power(q)
+        if pe is None:
+            raise ValueError(f"{q} is not a prime power")
+        self.q, (self.p, self.e) = q, pe
+        self.mod = gf_modulus(self.p, self.e) if self.e > 1 else [0, 1]
+        idx = np.arange(q)
+        self.digits = np.stack([(idx // self.p**t) % self.p for t in range(self.e)], axis=1)
+
+    def index(self, digits) -> int:
+        return int(sum(int(c) * self.p**t for t, c in enumerate(digits)))
+
+    def sub_table(self) -> np.ndarray:
+        """sub[i, j] = index of e_i - e_j."""
+        d = (self.digits[:, None, :] - self.digits[None, :, :]) % self.p
+        w = self.p ** np.arange(self.e)
+        return (d * w).sum(axis=2)
+
+    def mul(self, i: int, j: int) -> int:
+        a, b = self.digits[i], self.digits[j]
+        prod = [0] * (2 * self.e - 1)
+        for s_ in range(self.e):
+            for t in range(self.e):
+                prod[s_ + t] += int(a[s_]) * int(b[t])
+        for d in range(len(prod) - 1, self.e - 1, -1):  # t^d = t^(d-e) * (-(a_0 + ... ))
+            c = prod[d] % self.p
+            prod[d] = 0
+            for t in range(self.e):
+                prod[d - self.e + t] -= c * self.mod[t]
+        return self.index([v % self.p for v in prod[: self.e]])
+
+    def chi(self) -> np.ndarray:
+        """Quadratic character by index: 0 at 0, +1 on nonzero squares, else -1."""
+        sq = {self.mul(x, x) for x in range(1, self.q)}
+        c = np.array([1 if x in sq else -1 for x in range(self.q)], dtype=np.int64)
+        c[0] = 0
+        return c
+
+
+def paley_kind(m: int):
+    """('I', q) when q = m - 1 is a prime power = 3 (mod 4); else ('II', q) when
+    q = m/2 - 1 is a prime power = 1 (mod 4); else None."""
+    if m % 4:
+        return None
+    if m - 1 >= 3 and (m - 1) % 4 == 3 and prime_power(m - 1):
+        return ("I", m - 1)
+    q = m // 2 - 1
+    if q >= 5 and q % 4 == 1 and prime_power(q):
+        return ("II", q)
+    return None
+
+
+def _jacobsthal(q: int) -> np.ndarray:
+    f = GF(q)
+    return f.chi()[f.sub_table()]  # Q[i, j] = chi(e_i - e_j)
+
+
+def paley(m: int) -> np.ndarray:
+    """Hadamard matrix of order m by Paley's constructions (int8 +-1).
+    I  (q = m - 1 = 3 mod 4): S = [[0, 1^T], [-1, Q]], H = I + S.
+    II (q = m/2 - 1 = 1 mod 4): C = [[0, 1^T], [1, Q]] (symmetric), and
+       H = C (x) [[1, 1], [1, -1]] + I (x) [[1, -1], [-1, -1]]."""
+    kind = paley_kind(m)
+    if kind is None:
+        raise ValueError(f"no Paley construction of order {m}")
+    t, q = kind
+    qm = _jacobsthal(q)
+    if t == "I":
+        s_ = np.zeros((m, m), dtype=np.int64)
+        s_[0, 1:] = 1
+        s_[1:, 0] = -1
+        s_[1:, 1:] = qm
+        return (np.eye(m, dtype=np.int64) + s_).astype(np.int8)
+    c = np.zeros((q + 1, q + 1), dtype=np.int64)
+    c[0, 1:] = 1
+    c[1:, 0] = 1
+    c[1:, 1:] = qm
+    a = np.array([[1, 1], [1, -1]], dtype=np.int64)
+    b = np.array([[1, -1], [-1, -1]], dtype=np.int64)
+    return (np.kron(c, a) + np.kron(np.eye(q + 1, dtype=np.int64), b)).astype(np.int8)
+
+
+_OUTER_CACHE: dict = {}
+
+
+def outer_matrix(m: int) -> np.ndarray:
+    """H_m for the outer factor (paley28() for m = 28)."""
+    if m not in _OUTER_CACHE:
+        _OUTER_CACHE[m] = paley28() if m == 28 else paley(m)
+    return _OUTER_CACHE[m]
+
+
 def factor(n: int):
-    """Split n = m * 2^k with m in {1, 28}.  Returns (m, k) or raises."""
+    """Split n = m * 2^k: m = 1 for n = 2^k (k >= 1), else the outer order of
+    the rule above.  Returns (m, k) or raises."""
     if n < 2:
         raise ValueError(f"unsupported n={n}")
-    m = 28 if n % 28 == 0 else 1
-    p = n // m
-    if p & (p - 1):
-        raise ValueError(f"unsupported n={n}: not 2^k or 28*2^k")
-    k = p.bit_length() - 1
-    if m == 1 and k < 1:
-        raise ValueError(f"unsupported n={n}")
-    return m, k
+    o, v = n, 0
+    while o % 2 == 0:
+        o //= 2
+        v += 1
+    if o == 1:
+        return 1, v
+    for j in range(2, v + 1):
+        m = o << j
+        if m > MAX_OUTER:
+            break
+        if paley_kind(m) is not None:
+            return m, v - j
+    raise ValueError(f"unsupported n={n}: no Paley outer factor o*2^j <= {MAX_OUTER}")
 
 
 def hadamard(n: int) -> np.ndarray:
-    """Dense H_n (int8 +-1).  For n = 28*2^k it is the Kronecker product
-    H28 (x) H_{2^k} (READING), so that with i = a*2^k + b and j = a'*2^k + b',
-    H[i, j] = H28[a, a'] * Syl[b, b'].  Use only for small n."""
+    """Dense H_n (int8 +-1).  For n = m*2^k (m > 1) it is the Kronecker product
+    H_m (x) H_{2^k} (READING), so that with i = a*2^k + b and j = a'*2^k + b',
+    H[i, j] = H_m[a, a'] * Syl[b, b'].  Use only for small n."""
     m, k = factor(n)
     s = sylvester(k)
     if m == 1:
         return s
-    return np.kron(paley28().astype(np.int64), s.astype(np.int64)).astype(np.int8)
+    return np.kron(outer_matrix(m).astype(np.int64), s.astype(np.int64)).astype(np.int8)
 
 
 def hadamard_cols(n: int, j0: int, j1: int) -> np.ndarray:
@@ -146,9 +309,9 @@ def hadamard_cols(n: int, j0: int, j1: int) -> np.ndarray:
     bmask = (1 << k) - 1
     par = (np.bitwise_count((i[:, None] & bmask) & (j[None, :] & bmask)) & 1).astype(np.int64)
     blk = (1 - 2 * par).astype(np.float64)
-    if m == 28:
-        h28 = paley28().astype(np.float64)
-        blk *= h28[(i >> k)[:, None], (j >> k)[None, :]]
+    if m > 1:
+        hm = outer_matrix(m).astype(np.float64)
+        blk *= hm[(i >> k)[:, None], (j >> k)[None, :]]
     return blk
 
 
@@ -159,8 +322,8 @@ def hadamard_row(n: int, c: int) -> np.ndarray:
     bmask = (1 << k) - 1
     par = (np.bitwise_count((c & bmask) & (j & bmask)) & 1).astype(np.int64)
     row = 1 - 2 * par
-    if m == 28:
-        row = row * paley28().astype(np.int64)[c >> k, j >> k]
+    if m > 1:
+        row = row * outer_matrix(m).astype(np.int64)[c >> k, j >> k]
     return row.astype(np.int8)
 
 

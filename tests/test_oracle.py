@@ -66,7 +66,78 @@ def test_gf27_field_axioms():
         assert mul(mul(a, b), c) == mul(a, mul(b, c))
 
 
-SMALL_N = [2, 4, 8, 16, 32, 64, 128, 28, 56, 112, 224, 448]
+# Outer orders of the general rule (Paley I where m - 1 is a prime power = 3
+# mod 4, else Paley II), including the ones common model widths need:
+# 12 (24576), 20 (5120), 108 (13824, 27648), 140 (8960), 148 (18944) and 344
+# (11008 = 43 * 2^8, where 172 has no Paley construction).
+PALEY_M = [12, 20, 36, 44, 52, 60, 68, 76, 84, 100, 108, 124, 132, 140, 148, 164, 180, 344]
+
+
+@pytest.mark.parametrize("m", PALEY_M)
+def test_paley_orders_are_hadamard(m):
+    h = O.paley(m).astype(np.int64)
+    assert h.shape == (m, m) and set(np.unique(h)) == {-1, 1}
+    assert np.array_equal(h @ h.T, m * np.eye(m, dtype=np.int64))
+    kind, q = O.paley_kind(m)
+    if kind == "I":  # skew type: H + H^T = 2I, first row all +1
+        assert q == m - 1
+        assert np.array_equal(h + h.T, 2 * np.eye(m, dtype=np.int64))
+        assert np.all(h[0] == 1)
+    else:  # from a symmetric conference matrix: H is symmetric
+        assert q == m // 2 - 1
+        assert np.array_equal(h, h.T)
+
+
+def test_general_paley_reproduces_paley28():
+    """The general construction with the lexicographic-first modulus gives the
+    hand-written GF(27) matrix (modulus t^3 + 2t + 1) entry for entry."""
+    assert O.gf_modulus(3, 3) == [1, 2, 0, 1]
+    assert np.array_equal(O.paley(28), O.paley28())
+
+
+@pytest.mark.parametrize("q", [9, 25, 27, 49, 121, 125, 243, 343])
+def test_prime_power_field_axioms(q):
+    """GF(q) from the first irreducible modulus is a field: every nonzero
+    element has exactly one inverse, (q - 1)/2 nonzero squares, x^(q-1) = 1,
+    and the quadratic character is multiplicative (sampled)."""
+    f = O.GF(q)
+    one = 1
+    nz = range(1, q)
+    inv = {a: [b for b in nz if f.mul(a, b) == one] for a in nz}
+    assert all(len(v) == 1 for v in inv.values())
+    chi = f.chi()
+    assert int((chi == 1).sum()) == (q - 1) // 2 and chi[0] == 0
+    rng = np.random.default_rng(q)
+    for a, b in rng.integers(1, q, size=(60, 2)):
+        x = 1
+        for _ in range(q - 1):
+            x = f.mul(x, int(a))
+        assert x == 1
+        assert chi[f.mul(int(a), int(b))] == chi[a] * chi[b]
+
+
+def test_outer_factor_rule():
+    """n = o 2^v: m = o 2^j for the smallest j >= 2 with a Paley matrix of
+    order m <= 512; n = 2^v is pure Sylvester."""
+    want = {11008: (344, 5), 13824: (108, 7), 14336: (28, 9), 28672: (28, 10), 3584: (28, 7),
+            24576: (12, 11), 18944: (148, 7), 5120: (20, 8), 8960: (140, 6), 27648: (108, 8),
+            4096: (1, 12), 2: (1, 1), 12: (12, 0), 344: (344, 0), 28: (28, 0)}
+    for n, (m, k) in want.items():
+        assert O.factor(n) == (m, k)
+        assert m * (1 << k) == n
+    # minimality, by brute force over the powers of two
+    for n, (m, k) in want.items():
+        o = n
+        while o % 2 == 0:
+            o //= 2
+        if o > 1:
+            assert all(O.paley_kind(o << j) is None for j in range(2, (m // o).bit_length() - 1))
+    for n in (3, 6, 47 * 512, 23 * 4, 43 * 4):  # no construction within the bound
+        with pytest.raises(ValueError):
+            O.factor(n)
+
+
+SMALL_N = [2, 4, 8, 16, 32, 64, 128, 28, 56, 112, 224, 448, 12, 24, 40, 36, 72, 344]
 
 
 @pytest.mark.parametrize("n", SMALL_N)
@@ -75,7 +146,7 @@ def test_dense_hadamard_orthogonal(n):
     assert np.array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
 
 
-@pytest.mark.parametrize("n", [4096, 8192, 14336, 28672])
+@pytest.mark.parametrize("n", [4096, 8192, 14336, 28672, 11008, 13824, 18944, 24576])
 def test_large_hadamard_sampled_rows_orthogonal(n):
     rng = np.random.default_rng(n)
     rows = rng.choice(n, size=12, replace=False)
@@ -94,18 +165,18 @@ def test_textbook_fwht_equals_dense_product(n):
     assert np.allclose(O.fwht_textbook(x), y, rtol=0, atol=1e-12)
 
 
-@pytest.mark.parametrize("n", [28, 56, 112])
+@pytest.mark.parametrize("n", [28, 56, 112, 24, 40, 216, 344])
 def test_kronecker_two_stage_equals_dense(n):
-    """x.H for H = H28 (x) H_{2^k} equals: mix the 28 blocks of 2^k by H28
-    (block a feeds block a' with weight H28[a, a']), then a textbook FWHT
+    """x.H for H = H_m (x) H_{2^k} equals: mix the m blocks of 2^k by H_m
+    (block a feeds block a' with weight H_m[a, a']), then a textbook FWHT
     inside every block."""
-    k = (n // 28).bit_length() - 1
+    m, k = O.factor(n)
     x = np.random.default_rng(n).standard_normal((3, n))
-    h28 = O.paley28().astype(np.float64)
-    blocks = x.reshape(3, 28, 1 << k)
-    mixed = np.einsum("tab,ac->tcb", blocks, h28)
-    two_stage = O.fwht_textbook(mixed).reshape(3, n)
-    assert np.allclose(two_stage, O.rotate(x) * math.sqrt(n), rtol=0, atol=1e-12)
+    hm = O.outer_matrix(m).astype(np.float64)
+    blocks = x.reshape(3, m, 1 << k)
+    mixed = np.einsum("tab,ac->tcb", blocks, hm)
+    two_stage = O.fwht_textbook(mixed).reshape(3, n) if k else mixed.reshape(3, n)
+    assert np.allclose(two_stage, O.rotate(x) * math.sqrt(n), rtol=0, atol=1e-9)
 
 
 def test_brute_force_n2_n4():
