@@ -4,9 +4,10 @@ oracle's quant_asym_zint.
 Decisions taken in binary32 on both sides can part only next to a rounding
 boundary: the zero-point z = rint(-mn/s) may differ by one where -mn/s lies
 within 1e-4 of a half-integer, and a code may differ by one where y/s lies
-within 1e-4 of one (at most 1e-4 of the elements).  Codes are compared as
-levels m = q - z, which a shifted zero-point leaves unchanged except where one
-side clamps.
+within 1e-4 of one (at most 1e-4 of the elements).  The band widens per token
+where binary32 cannot place a position that closely (parity.position_window:
+a short row with a huge outlier).  Codes are compared as levels m = q - z,
+which a shifted zero-point leaves unchanged except where one side clamps.
 """
 
 import math
@@ -20,6 +21,7 @@ torch = pytest.importorskip("torch")
 import oracle as O  # noqa: E402
 import rotation_activation_quantization_amd as R  # noqa: E402
 import signrot_workloads as W  # noqa: E402
+from parity import position_window  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 BOUNDARY = 1e-4
@@ -38,8 +40,8 @@ def dev(bits):
     return torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)[:t, :n]
 
 
-def near_half(p):
-    return np.abs(p - np.floor(p) - 0.5) < BOUNDARY
+def near_half(p, band=BOUNDARY):
+    return np.abs(p - np.floor(p) - 0.5) < band
 
 
 def compare_zint(y, codes, scale, zero, label):
@@ -50,15 +52,17 @@ def compare_zint(y, codes, scale, zero, label):
     mn = y.min(axis=1)
     zpos = -mn / s64
     dz = zero - z32
-    assert np.all((dz == 0) | (near_half(zpos) & (np.abs(dz) == 1))), label
+    win = position_window(y, s64, integer_zero=True)
+    assert np.all((dz == 0) | (near_half(zpos, win) & (np.abs(dz) == 1))), label
     q = O.unpack_int4(codes).astype(np.int64)
     m_gpu = q - zero[:, None].astype(np.int64)
     m_ora = q32.astype(np.int64) - z32[:, None].astype(np.int64)
     diff = m_gpu != m_ora
     pos = y / s64[:, None]
     at_boundary = near_half(pos)
+    in_band = near_half(pos, win[:, None])
     clamped = (q == 0) | (q == 15) | (q32 == 0) | (q32 == 15)
-    allowed = (at_boundary & (np.abs(m_gpu - m_ora) <= 1)) | ((dz != 0)[:, None] & clamped)
+    allowed = (in_band & (np.abs(m_gpu - m_ora) <= 1)) | ((dz != 0)[:, None] & clamped)
     assert np.all(~diff | allowed), label
     assert int((diff & at_boundary).sum()) <= math.ceil(BOUNDARY * y.size), label
     return int(diff.sum()), int((dz != 0).sum())
