@@ -15,14 +15,22 @@
  * and maximum, an asymmetric INT4 code with a zero-point (explainer,
  * paragraphs on the quantizer and on symmetric versus asymmetric quantizers).
  *
- * Hadamard order.  n = 2^k (1 <= k <= 15) uses the Sylvester matrix in natural
- * order, H[i][j] = (-1)^popcount(i & j).  n = 28 * 2^k (0 <= k <= 10) uses
- * H = H28 (x) H_{2^k} with index i = a * 2^k + b (a < 28, b < 2^k), where H28
- * is Paley's construction I over GF(27) = GF(3)[t]/(t^3 + 2t + 1): H28 = I + S,
- * S the Jacobsthal matrix of the quadratic character bordered by a row of +1
- * and a column of -1.  The pages only fix "a Hadamard matrix"; these are the
- * library's choices.  Orientation: y_j = sum_i x_i H[i][j] (x is a row
- * vector; the outlier at channel c reaches the outputs through row c of H).
+ * Hadamard order (n <= 32768).  n = 2^k (k >= 1) uses the Sylvester matrix in
+ * natural order, H[i][j] = (-1)^popcount(i & j).  Any other n = o * 2^v (o
+ * odd) uses H = H_m (x) H_{2^k} with index i = a * 2^k + b (a < m, b < 2^k),
+ * where m = o * 2^j for the smallest j >= 2 for which Paley's construction I
+ * (q = m - 1 a prime power = 3 mod 4: H_m = I + S, S the Jacobsthal matrix of
+ * the quadratic character of GF(q) bordered by a row of +1 and a column of -1)
+ * or, failing that, construction II (q = m/2 - 1 a prime power = 1 mod 4:
+ * H_m = C (x) [[1,1],[1,-1]] + I (x) [[1,-1],[-1,-1]], C the symmetric
+ * conference matrix) exists with m <= 512.  GF(p^e) is GF(p)[t] modulo the
+ * first monic irreducible polynomial in lexicographic order of its
+ * coefficients.  So 28 * 2^k uses H28 over GF(27) = GF(3)[t]/(t^3 + 2t + 1),
+ * 13824 = 108 * 2^7 uses construction I over GF(107), and 11008 = 344 * 2^5
+ * uses construction I over GF(7^3) (172 * 2^6 has no Paley factor).  The
+ * pages only ask for some Hadamard matrix; these are the library's choices.
+ * Orientation: y_j = sum_i x_i H[i][j] (x is a row vector; the outlier at
+ * channel c reaches the outputs through row c of H).
  *
  * Conventions shared by every call:
  *   - All sizes are element counts.  Device pointers are plain HIP device
@@ -53,12 +61,16 @@ extern "C" {
 typedef enum {
   SIGNROT_OK = 0,
   SIGNROT_EINVAL = -1,          /* bad pointer, size, stride or alignment   */
-  SIGNROT_EUNSUPPORTED_N = -2,  /* n is neither 2^k nor 28 * 2^k in range    */
+  SIGNROT_EUNSUPPORTED_N = -2,  /* n has no factorisation of the rule above  */
   SIGNROT_EHIP = -3             /* a HIP runtime call or launch failed       */
 } signrot_status;
 
-/* 1 if n = 2^k (1 <= k <= 15) or n = 28 * 2^k (0 <= k <= 10), else 0. */
+/* 1 if n factors by the rule above (n <= 32768), else 0. */
 int signrot_supported_n(int64_t n);
+
+/* The outer order m of n by that rule (1 for n = 2^k), or 0 when n is
+ * unsupported. */
+int signrot_outer_order(int64_t n);
 
 /*
  * Calibration (abstract: one calibration forward pass; explainer, paragraph
@@ -249,6 +261,13 @@ const char* signrot_last_error(void);
  * out[784].  Lets a test compare it with an independently built table.
  */
 int signrot_debug_h28(int8_t* out);
+
+/*
+ * The library's outer factor H_m (m = 28 or any Paley order of the rule above,
+ * m <= 512), row-major, entries +1/-1, written to host memory out[m * m].
+ * Host-only (no GPU needed).  SIGNROT_EINVAL when m has no construction.
+ */
+int signrot_debug_outer(int m, int8_t* out);
 
 /* Which kernel variant signrot_rotate_quant_int4 would launch for n (a
  * static string naming it), or NULL when n is unsupported. */

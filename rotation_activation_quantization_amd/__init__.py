@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.signrot_last_error.restype = ctypes.c_char_p
     L.signrot_debug_h28.argtypes = [vp]
     L.signrot_debug_h28.restype = ctypes.c_int
+    L.signrot_debug_outer.argtypes = [ctypes.c_int, vp]
+    L.signrot_debug_outer.restype = ctypes.c_int
+    L.signrot_outer_order.argtypes = [i64]
+    L.signrot_outer_order.restype = ctypes.c_int
     L.signrot_kernel_name.argtypes = [i64]
     L.signrot_kernel_name.restype = ctypes.c_char_p
     _lib = L
@@ -87,6 +91,8 @@ EXPORTED = (
     "signrot_strerror",
     "signrot_last_error",
     "signrot_debug_h28",
+    "signrot_debug_outer",
+    "signrot_outer_order",
     "signrot_kernel_name",
 )
 
@@ -105,6 +111,18 @@ def supported_n(n: int) -> bool:
 def kernel_name(n: int) -> str | None:
     r = lib().signrot_kernel_name(int(n))
     return r.decode() if r else None
+
+
+def outer_order(n: int) -> int:
+    """The outer Hadamard order m of n = m * 2^k (1 for n = 2^k, 0 if unsupported)."""
+    return int(lib().signrot_outer_order(int(n)))
+
+
+def debug_outer(m: int):
+    """The library's outer factor H_m as an m x m list of +-1 rows (host only)."""
+    buf = (ctypes.c_int8 * (m * m))()
+    check(lib().signrot_debug_outer(int(m), ctypes.addressof(buf)), "signrot_debug_outer")
+    return [list(buf[r * m:(r + 1) * m]) for r in range(m)]
 
 
 def debug_h28():

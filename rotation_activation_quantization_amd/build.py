@@ -22,6 +22,7 @@ SOURCES = [
     "calib_dequant.hip",
     "linear.hip",
     "hadamard28.cpp",
+    "outer.cpp",
 ]
 
 ARCH = "gfx950"

@@ -41,22 +41,58 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 Shape factor_n(int64_t n) {
   Shape s;
   if (n < 2 || n > 32768) return s;
-  int64_t p = n;
-  bool m28 = false;
-  if (n % 28 == 0) {
-    m28 = true;
-    p = n / 28;
+  int64_t o = n;
+  int v = 0;
+  while ((o & 1) == 0) {
+    o >>= 1;
+    ++v;
   }
-  if (p & (p - 1)) return s;
+  int m = 1;
+  if (o > 1) {
+    m = outer_order_for(static_cast<int>(o), v);
+    if (m == 0) return s;
+  }
+  const int64_t p = n / m;
   int k = 0;
   while ((int64_t{1} << k) < p) ++k;
-  if (m28 && k > 10) return s;
-  if (!m28 && (k < 1 || k > 15)) return s;
+  if (m == 1 && k < 1) return s;
   s.n = static_cast<int>(n);
   s.k = k;
-  s.m28 = m28;
+  s.m = m;
+  s.m28 = (m == 28);
   s.ok = true;
   return s;
+}
+
+const uint32_t* outer_mask_device(int m, hipError_t* err) {
+  *err = hipSuccess;
+  static std::mutex mu;
+  static std::vector<std::vector<std::pair<int, uint32_t*>>> per_dev;
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(per_dev.size())) per_dev.resize(dev + 1);
+  for (auto& e : per_dev[dev])
+    if (e.first == m) return e.second;
+  std::vector<uint32_t> mask;
+  if (m == 28) {  // h28(): one word per row
+    mask.assign(h28().rowmask, h28().rowmask + 28);
+  } else {
+    const OuterTable* t = outer_table(m);
+    if (!t) {
+      *err = hipErrorInvalidValue;
+      return nullptr;
+    }
+    mask = t->mask;
+  }
+  uint32_t* ptr = nullptr;
+  if ((*err = hipMalloc(&ptr, mask.size() * sizeof(uint32_t))) != hipSuccess) return nullptr;
+  if ((*err = hipMemcpy(ptr, mask.data(), mask.size() * sizeof(uint32_t), hipMemcpyHostToDevice)) != hipSuccess) {
+    (void)hipFree(ptr);
+    return nullptr;
+  }
+  per_dev[dev].push_back({m, ptr});
+  return ptr;
 }
 
 int device_cu_count() {
@@ -87,7 +123,9 @@ const char* signrot_strerror(int status) {
   switch (status) {
     case SIGNROT_OK: return "ok";
     case SIGNROT_EINVAL: return "invalid argument";
-    case SIGNROT_EUNSUPPORTED_N: return "unsupported n (need 2^k, 1<=k<=15, or 28*2^k, 0<=k<=10)";
+    case SIGNROT_EUNSUPPORTED_N:
+      return "unsupported n (need n <= 32768, n = 2^k with k >= 1, or n = m * 2^k with m = o * 2^j the smallest "
+             "Paley order <= 512 for the odd part o of n)";
     case SIGNROT_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -98,6 +136,25 @@ const char* signrot_last_error(void) { return g_last_error; }
 int signrot_debug_h28(int8_t* out) {
   if (!out) return fail_einval("out is NULL");
   memcpy(out, h28().h, 28 * 28);
+  return SIGNROT_OK;
+}
+
+int signrot_outer_order(int64_t n) {
+  const Shape sh = factor_n(n);
+  return sh.ok ? sh.m : 0;
+}
+
+int signrot_debug_outer(int m, int8_t* out) {
+  g_last_error[0] = '\0';
+  if (!out) return fail_einval("out is NULL");
+  if (m == 28) {
+    memcpy(out, h28().h, 28 * 28);
+    return SIGNROT_OK;
+  }
+  if (m < 2 || m > kMaxOuter) return fail_einval("m out of range");
+  const OuterTable* t = outer_table(m);
+  if (!t) return fail_einval("no Paley construction of order m");
+  memcpy(out, t->h.data(), static_cast<size_t>(m) * m);
   return SIGNROT_OK;
 }
 
@@ -177,6 +234,13 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   a.inv_sqrt_n = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  {
+    hipError_t he = hipSuccess;
+    a.m = sh.m;
+    a.hw = (sh.m + 31) / 32;
+    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
+    if (sh.m > 1 && !a.hm) return fail_hip(he, "outer Hadamard factor table");
+  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, st) : launch_rq_generic(a, st);
   if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4 launch");
@@ -224,6 +288,13 @@ int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int
   a.form_neg = sigma < 0 ? 1 : 0;
   a.zint = zint;
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  {
+    hipError_t he = hipSuccess;
+    a.m = sh.m;
+    a.hw = (sh.m + 31) / 32;
+    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
+    if (sh.m > 1 && !a.hm) return fail_hip(he, "outer Hadamard factor table");
+  }
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (rq_fast_supports(sh.n, sh.k, sh.m28)) {
     const hipError_t e = launch_rq_fast(a, st);
@@ -298,6 +369,16 @@ int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld
   a.inv_sqrt_n = static_cast<float>(1.0 / sqrt(static_cast<double>(n)));
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
+  {
+    hipError_t he = hipSuccess;
+    a.m = sh.m;
+    a.hw = (sh.m + 31) / 32;
+    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
+    if (sh.m > 1 && !a.hm) {
+      (void)hipFreeAsync(scratch, s);
+      return fail_hip(he, "outer Hadamard factor table");
+    }
+  }
   e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, s) : launch_rq_generic(a, s);
   const hipError_t ef = hipFreeAsync(scratch, s);
   if (e == hipSuccess) e = ef;

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kCalThreads) void cal_argmax_kernel(const uint16_t*
 }
 
 // Fills d[j] = sigma * H[c][j]; also records the bf16 bits of M_c in scratch[1].
-__global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int m28,
-                                H28Masks masks, unsigned long long* scratch, int8_t* d) {
+__global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int m, int hw,
+                                const uint32_t* hm, unsigned long long* scratch, int8_t* d) {
   const unsigned long long key = scratch[0];
   const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
   const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
@@ -64,7 +64,7 @@ __global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int
   const int bmask = (1 << k) - 1;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
     uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-    if (m28) bit ^= (masks.m[c >> k] >> (j >> k)) & 1u;
+    if (m > 1) bit ^= (hm[(c >> k) * hw + ((j >> k) >> 5)] >> ((j >> k) & 31)) & 1u;
     d[j] = (bit ^ neg) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) scratch[1] = mbits;
@@ -72,11 +72,11 @@ __global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int
 
 // d[j] = sigma * H[c][j] for a given (c, sigma): the same entries as the
 // calibration fill.
-__global__ void sign_fill_kernel(int n, int k, int m28, H28Masks masks, int c, int neg, int8_t* d) {
+__global__ void sign_fill_kernel(int n, int k, int m, int hw, const uint32_t* hm, int c, int neg, int8_t* d) {
   const int bmask = (1 << k) - 1;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
     uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-    if (m28) bit ^= (masks.m[c >> k] >> (j >> k)) & 1u;
+    if (m > 1) bit ^= (hm[(c >> k) * hw + ((j >> k) >> 5)] >> ((j >> k) & 31)) & 1u;
     d[j] = (bit ^ static_cast<uint32_t>(neg)) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
   }
 }
@@ -113,11 +113,11 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const
                      x, tokens, static_cast<int64_t>(sh.n), ld, scratch);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  H28Masks masks;
-  for (int i = 0; i < 28; ++i) masks.m[i] = h28().rowmask[i];
+  const uint32_t* hm = nullptr;
+  if (sh.m > 1 && !(hm = outer_mask_device(sh.m, &e))) return e;
   const int fill_blocks = (sh.n + 255) / 256;
-  hipLaunchKernelGGL(cal_fill_kernel, dim3(fill_blocks), dim3(256), 0, s, x, ld, sh.n, sh.k,
-                     sh.m28 ? 1 : 0, masks, scratch, d_out);
+  hipLaunchKernelGGL(cal_fill_kernel, dim3(fill_blocks), dim3(256), 0, s, x, ld, sh.n, sh.k, sh.m,
+                     (sh.m + 31) / 32, hm, scratch, d_out);
   return hipGetLastError();
 }
 
@@ -134,10 +134,12 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float*
 }
 
 hipError_t launch_sign_fill(const Shape& sh, int c, int neg, int8_t* d, hipStream_t s) {
-  H28Masks masks;
-  for (int i = 0; i < 28; ++i) masks.m[i] = h28().rowmask[i];
+  hipError_t e = hipSuccess;
+  const uint32_t* hm = nullptr;
+  if (sh.m > 1 && !(hm = outer_mask_device(sh.m, &e))) return e;
   const int blocks = (sh.n + 255) / 256;
-  hipLaunchKernelGGL(sign_fill_kernel, dim3(blocks), dim3(256), 0, s, sh.n, sh.k, sh.m28 ? 1 : 0, masks, c, neg, d);
+  hipLaunchKernelGGL(sign_fill_kernel, dim3(blocks), dim3(256), 0, s, sh.n, sh.k, sh.m, (sh.m + 31) / 32, hm, c, neg,
+                     d);
   return hipGetLastError();
 }
 

@@ -11,12 +11,17 @@ namespace signrot {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Sign bit (1 = negative) of entry j of sigma * (row c of H), H = H28 (x) H_{2^k}
-// or the Sylvester matrix alone.
+// Sign bit (1 = negative) of H_m[r][col] from the mask table (words per row).
+__device__ __forceinline__ uint32_t outer_negbit(const uint32_t* hm, int words, int r, int col) {
+  return (hm[r * words + (col >> 5)] >> (col & 31)) & 1u;
+}
+
+// Sign bit (1 = negative) of entry j of row c of H, H = H_m (x) H_{2^k} or
+// the Sylvester matrix alone (m = 1).
 __device__ __forceinline__ uint32_t hrow_negbit(const RqArgs& a, int c, int j) {
   const int bmask = (1 << a.k) - 1;
   uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-  if (a.m28) bit ^= (a.h28mask[c >> a.k] >> (j >> a.k)) & 1u;
+  if (a.m > 1) bit ^= outer_negbit(a.hm, a.hw, c >> a.k, j >> a.k);
   return bit;
 }
 
@@ -27,10 +32,10 @@ __device__ __forceinline__ uint32_t hrow_negbit(const RqArgs& a, int c, int j) {
 //
 // Decoding: over b (the Sylvester index) the row of a Sylvester matrix is the
 // character (-1)^popcount(c_b & b), so bit t of c_b is read off the sign
-// change between b = 0 and b = 2^t.  Over a (the order-28 index) the row of
-// H28 normalised by its first entry is unique, so c_a is found by matching
-// the 28 entries d[a' 2^k], again normalised by d[0].  Then every entry is
-// checked.
+// change between b = 0 and b = 2^t.  Over a (the outer index) the row of H_m
+// normalised by its first entry is unique (the rows are orthogonal), so c_a is
+// found by matching the m entries d[a' 2^k], again normalised by d[0]; the
+// threads share the candidate rows.  Then every entry is checked.
 struct DForm {
   int structured;  // 1 if d = sigma * H[c][.]
   int c;           // outlier channel
@@ -40,29 +45,28 @@ struct DForm {
 __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, int* sh_scratch) {
   const int tid = threadIdx.x;
   auto dbit = [&](int j) -> uint32_t { return (dbits[j >> 5] >> (j & 31)) & 1u; };
+  if (tid == 0) sh_scratch[3] = a.m > 1 ? -1 : 0;
+  __syncthreads();
+  const uint32_t d0 = dbit(0);
+  if (a.m > 1) {
+    for (int r = tid; r < a.m; r += blockDim.x) {
+      const uint32_t r0 = outer_negbit(a.hm, a.hw, r, 0);
+      int ok = 1;
+      for (int ap = 0; ap < a.m && ok; ++ap)
+        ok = ((dbit(ap << a.k) ^ d0) == (outer_negbit(a.hm, a.hw, r, ap) ^ r0));
+      if (ok) sh_scratch[3] = r;  // at most one row matches
+    }
+  }
+  __syncthreads();
   if (tid == 0) {
-    const uint32_t d0 = dbit(0);
     int cb = 0;
     for (int t = 0; t < a.k; ++t)
       if (dbit(1 << t) != d0) cb |= 1 << t;
-    int ca = 0;
-    int found = 1;
-    if (a.m28) {
-      found = 0;
-      for (int r = 0; r < 28 && !found; ++r) {
-        const uint32_t r0 = a.h28mask[r] & 1u;
-        int ok = 1;
-        for (int ap = 0; ap < 28; ++ap) {
-          const uint32_t want = dbit(ap << a.k) ^ d0;
-          const uint32_t have = ((a.h28mask[r] >> ap) & 1u) ^ r0;
-          if (want != have) { ok = 0; break; }
-        }
-        if (ok) { ca = r; found = 1; }
-      }
-    }
+    const int found = sh_scratch[3] >= 0;
+    const int ca = found ? sh_scratch[3] : 0;
     const int c = (ca << a.k) | cb;
     // sigma: d_0 = sigma * H[c][0]
-    const uint32_t neg = d0 ^ (a.m28 ? (a.h28mask[ca] & 1u) : 0u);
+    const uint32_t neg = d0 ^ (a.m > 1 ? outer_negbit(a.hm, a.hw, ca, 0) : 0u);
     sh_scratch[0] = found;
     sh_scratch[1] = c;
     sh_scratch[2] = static_cast<int>(neg);

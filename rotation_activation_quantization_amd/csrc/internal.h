@@ -4,16 +4,39 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 namespace signrot {
 
-// Factorisation n = m * 2^k with m in {1, 28}.
+// Factorisation n = m * 2^k (n <= 32768): m = 1 for n = 2^k (k >= 1);
+// otherwise n = o * 2^v with o odd and m = o * 2^j, the smallest j >= 2 for
+// which a Paley matrix of order m <= kMaxOuter exists (m = 28 for o = 7).
+constexpr int kMaxOuter = 512;
 struct Shape {
   int n = 0;
   int k = 0;
-  bool m28 = false;
+  int m = 1;
+  bool m28 = false;  // m == 28: the order-28 kernels and h28()
   bool ok = false;
 };
 Shape factor_n(int64_t n);
+
+// Outer factors other than order 28's hand-built table: Paley's
+// constructions I and II (outer.cpp).  outer_order_for returns m or 0;
+// outer_table returns the cached host table (nullptr when no construction);
+// mask[r * words + w] has bit b set iff H_m[r][32 w + b] == -1.
+struct OuterTable {
+  int m = 0;
+  int words = 0;
+  std::vector<int8_t> h;  // m x m, row-major
+  std::vector<uint32_t> mask;
+};
+int outer_order_for(int odd, int v);
+const OuterTable* outer_table(int m);
+// The mask table of H_m on the current device: copied there on first use
+// (hipMalloc + hipMemcpy, not capturable) and kept until the process ends.
+// nullptr (with *err set) on failure.
+const uint32_t* outer_mask_device(int m, hipError_t* err);
 
 // The library's order-28 Hadamard matrix (Paley construction I over GF(27)),
 // built once on the host.  rowmask[a] has bit a' set iff H28[a][a'] == -1.
@@ -49,6 +72,9 @@ struct RqArgs {
   int form_neg;        // 1 when sigma = -1
   int zint;            // 1: integer zero-point z = rint(-mn / s), q = clamp(rint(y / s) + z, 0, 15)
   uint32_t h28mask[28];
+  int m;                 // outer order (1: none)
+  int hw;                // 32-bit words per mask row of H_m
+  const uint32_t* hm;    // device mask table of H_m (m > 1), see OuterTable
 };
 
 // Launchers; each returns the hipError_t of the launch.

@@ -2,11 +2,14 @@
 //
 // One workgroup per token row (persistent: a workgroup walks rows with a grid
 // stride).  The row is widened to binary32 in LDS; the order-28 mix (when
-// n = 28 * 2^k) runs column by column, one thread per column b; the 2^k
-// Walsh-Hadamard transform runs as radix-2 butterfly passes over LDS with a
-// barrier between passes; the flip, the min/max reduction, the quantizer and
-// the nibble packing follow.  It handles every supported n (2 .. 32768) and
-// is the reference HIP path for the shapes that have no specialised kernel.
+// n = 28 * 2^k) runs column by column, one thread per column b, in LDS; a
+// mix of another outer order m (n = m * 2^k, H_m a Paley matrix) reads the
+// bf16 row from global memory and writes the mixed row to LDS, 16 outputs per
+// work item; the 2^k Walsh-Hadamard transform runs as radix-2 butterfly
+// passes over LDS with a barrier between passes; the flip, the min/max
+// reduction, the quantizer and the nibble packing follow.  It handles every
+// supported n and is the HIP path for the shapes that have no specialised
+// kernel.
 //
 // Method: explainer "SignRot for 4-bit LLM quantization -- Sign-adjusted
 // Hadamard rotation", paragraphs on rotation (entries +-1/sqrt(n), fast
@@ -66,9 +69,15 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(RqArgs a) {
   __syncthreads();
   const DForm form = decode_d_form(a, dbits, scratch);
 
+  // Outer orders other than 28 mix straight from the bf16 row in global
+  // memory (the mix writes every entry of the LDS row, so no copy is needed).
+  const bool outer_general = a.m > 1 && !a.m28;
+
   for (int64_t t = blockIdx.x; t < a.tokens; t += gridDim.x) {
     const uint16_t* xr = a.x + t * a.ld;
-    if ((n & 7) == 0) {
+    if (outer_general) {
+      // nothing to widen
+    } else if ((n & 7) == 0) {
       for (int i = tid * 8; i < n; i += nt * 8) {
         const uint4 v = *reinterpret_cast<const uint4*>(xr + i);
         row[i + 0] = bf16_lo(v.x); row[i + 1] = bf16_hi(v.x);
@@ -83,8 +92,12 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(RqArgs a) {
     // SignRot form: take the outlier channel out of the transform; its
     // contribution after the flip is the constant sigma * x_c.
     if (form.structured && tid == 0) {
-      s_xc = row[form.c];
-      row[form.c] = 0.0f;
+      if (outer_general) {
+        s_xc = __uint_as_float(static_cast<uint32_t>(xr[form.c]) << 16);
+      } else {
+        s_xc = row[form.c];
+        row[form.c] = 0.0f;
+      }
     }
     __syncthreads();
     const float xc = form.structured ? s_xc : 0.0f;
@@ -106,6 +119,29 @@ __global__ __launch_bounds__(kThreads) void rq_generic_kernel(RqArgs a) {
         }
 #pragma unroll
         for (int ap = 0; ap < 28; ++ap) row[ap * B + b] = out[ap];
+      }
+      __syncthreads();
+    } else if (outer_general) {
+      // Z[a'][b] = sum_a H_m[a][a'] X[a][b], 16 consecutive a' per work item;
+      // the outlier entry (when d has the SignRot form) counts as zero.
+      const int groups = (a.m + 15) >> 4;
+      const int skip = form.structured ? form.c : -1;
+      for (int it = tid; it < groups * B; it += nt) {
+        const int ap0 = (it / B) << 4;
+        const int b = it - (it / B) * B;
+        float acc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+        for (int r = 0; r < a.m; ++r) {
+          const int idx = r * B + b;
+          const float v = idx == skip ? 0.0f : __uint_as_float(static_cast<uint32_t>(xr[idx]) << 16);
+          const uint32_t sg = a.hm[r * a.hw + (ap0 >> 5)] >> (ap0 & 31);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) acc[j] += ((sg >> j) & 1u) ? -v : v;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (ap0 + j < a.m) row[(ap0 + j) * B + b] = acc[j];
       }
       __syncthreads();
     }

@@ -62,6 +62,10 @@ WORKLOADS = {
     # n = 28 * 2^10 (LLaMA3-70B), Student-t(3)*0.4, +M in 15%, 8 mild channels x20
     "n28672_t8192": Workload("n28672_t8192", 4, 28672, 8192, "t", 0.4, df=3, p_outlier=0.15, m_lo=1000, m_hi=3000,
                      mild_channels=8, mild_factor=20.0, calib_tokens=512),
+    # n = 43 * 2^8 (LLaMA-2-7B down_proj input; outer Paley factor of order 344),
+    # N(0, 0.7), +M in 20% of tokens
+    "n11008_t8192": Workload("n11008_t8192", 6, 11008, 8192, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
+                       calib_tokens=256),
     # decode-shaped batches with the n = 14336 law (1, 4 or 16 tokens per call)
     "n14336_decode": Workload("n14336_decode", 5, 14336, 16, "normal", 0.7, p_outlier=0.20, m_lo=800, m_hi=2500,
                      calib_tokens=256, extra={"batches": (1, 4, 16), "repeats": 10000}),

@@ -40,16 +40,46 @@ def test_library_exports_every_declared_symbol(L):
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
 
 
+def _oracle_supports(n):
+    try:
+        O.factor(n)
+        return True
+    except ValueError:
+        return False
+
+
 def test_supported_n_table(L):
     good = [2 ** k for k in range(1, 16)] + [28 * 2 ** k for k in range(0, 11)]
+    good += [12, 20, 24, 40, 344, 5120, 8960, 11008, 13824, 18944, 24576, 27648]
     for n in good:
         assert L.signrot_supported_n(n) == 1, n
-    for n in [0, 1, -4, 3, 6, 12, 14, 20, 11008, 65536, 28 * 2048, 28 * 3, 100]:
+    for n in [0, 1, -4, 3, 6, 14, 30, 65536, 28 * 2048, 43 * 4, 92 * 2, 236 * 8]:
         assert L.signrot_supported_n(n) == 0, n
 
 
-def test_library_h28_equals_oracle_h28():
-    assert np.array_equal(np.array(R.debug_h28(), dtype=np.int8), O.paley28())
+def test_supported_n_agrees_with_the_oracle_rule(L):
+    """The library accepts n <= 32768 exactly when the oracle's factor rule
+    finds an outer order, and then picks the same one (the two implement the
+    rule independently: C++ and numpy)."""
+    for n in list(range(0, 4097)) + list(range(4100, 32769, 4)) + [32772, 40960, 57344]:
+        want = n <= 32768 and _oracle_supports(n)
+        assert L.signrot_supported_n(n) == int(want), n
+        if want:
+            assert R.outer_order(n) == O.factor(n)[0], n
+
+
+@pytest.mark.parametrize("m", [12, 20, 28, 36, 44, 52, 60, 68, 76, 84, 100, 108, 124, 132, 140, 148, 164, 180,
+                               196, 244, 344, 500])
+def test_library_outer_factor_equals_oracle(m):
+    """Paley I and II outer factors built by the library's C++ field
+    arithmetic against the oracle's numpy construction, entry by entry."""
+    assert np.array_equal(R.debug_outer(m), O.outer_matrix(m).astype(np.int8))
+
+
+def test_debug_outer_rejects_orders_without_a_construction(L):
+    buf = (ctypes.c_int8 * (516 * 516))()
+    for m in (0, 1, 2, 16, 92, 236, 508, 600):
+        assert L.signrot_debug_outer(m, buf) == R.SIGNROT_EINVAL, m
 
 
 def test_strerror_texts(L):
@@ -66,7 +96,7 @@ def _rq(L, x=FAKE, t=4, n=4096, ld=4096, d=FAKE, codes=FAKE, scale=FAKE, zero=FA
 
 def test_rotate_quant_argument_errors(L):
     assert _rq(L, n=6) == R.SIGNROT_EUNSUPPORTED_N
-    assert _rq(L, n=11008) == R.SIGNROT_EUNSUPPORTED_N
+    assert _rq(L, n=43 * 4) == R.SIGNROT_EUNSUPPORTED_N  # no Paley matrix of order 172
     assert "unsupported" in L.signrot_last_error().decode()
     assert _rq(L, t=-1) == R.SIGNROT_EINVAL
     assert _rq(L, ld=4095) == R.SIGNROT_EINVAL

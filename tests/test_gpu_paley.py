@@ -1,0 +1,196 @@
+"""Parity of the HIP path with the oracle at widths n = m * 2^k whose outer
+factor H_m is a Paley matrix of an order other than 28 (Paley I for
+m - 1 = 11, 19, 43, 107, 139, 343, ...; Paley II for m / 2 - 1 = 5, 9, 13,
+49, 73, ...).  These shapes run the generic kernel; the oracle builds H_m by
+its own finite-field arithmetic (numpy), the library by its own (C++).
+
+Tolerances are the ones in parity.py (rotated values within 1e-5 of the
+token's max |y|, scale and zero-point within 1e-6, codes bit-exact except at
+a rounding boundary).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import rotation_activation_quantization_amd as R  # noqa: E402
+import signrot_workloads as W  # noqa: E402
+from parity import compare, expected  # noqa: E402
+from test_gpu_zint import compare_zint  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+# (n, (m, k)): small orders that still span several outer blocks, and the
+# MLP widths of common models (11008, 13824, 18944) plus two-factor widths
+WIDTHS = [12, 20, 24, 40, 72, 344, 1000, 5120, 8960, 11008, 13824, 18944, 24576]
+CHEAP = [n for n in WIDTHS if n <= 8960]
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(bits, ld=None):
+    t, n = bits.shape
+    ld = (n + 7) // 8 * 8 if ld is None else ld
+    buf = np.zeros((max(t, 1), ld), np.uint16)
+    buf[:t, :n] = bits
+    return torch.from_numpy(buf.view(np.int16)).cuda().view(torch.bfloat16)[:t, :n]
+
+
+def to_np(outs):
+    return [o.cpu().numpy() if o is not None else None for o in outs]
+
+
+def test_widths_use_the_intended_outer_orders():
+    for n in WIDTHS:
+        m, k = O.factor(n)
+        assert m not in (1, 28) and R.outer_order(n) == m, n
+        assert R.kernel_name(n) == "rq_generic", n
+
+
+@pytest.mark.parametrize("n", WIDTHS)
+def test_calibrate_bit_exact(n):
+    bits = W.random_rows(40, n, seed=n + 1, scale=0.9)
+    c = (n * 5) // 7
+    bits[::3, c] = W.f32_to_bf16_bits(np.array([-1400.0], np.float32))[0]
+    say(f"[gpu] paley calibrate n={n} m={R.outer_order(n)}")
+    d, c_g, t, mc = R.calibrate(dev(bits))
+    ref = O.calibrate(bits)
+    assert (c_g, t, mc) == (ref["c"], ref["t"], np.float32(ref["m_c"]))
+    assert c_g == c
+    assert np.array_equal(d.cpu().numpy(), ref["d"])
+
+
+@pytest.mark.parametrize("n", WIDTHS)
+def test_rotate_quant_matches_oracle(n):
+    """37 tokens with a planted outlier in a third of them; d from the
+    oracle's calibration (the SignRot form), and for the cheaper widths also a
+    random sign vector and d = 1 (plain Hadamard)."""
+    t = 37
+    bits = W.random_rows(t, n, seed=n, scale=1.0)
+    c = (n * 7 // 11) % n
+    bits[::3, c] = W.f32_to_bf16_bits(np.array([900.0], np.float32))[0]
+    ds = [("signrot-d", O.calibrate(bits)["d"])]
+    if n in CHEAP:
+        g = np.random.default_rng([7, n])
+        ds.append(("random-d", np.where(g.random(n) < 0.5, -1, 1).astype(np.int8)))
+        ds.append(("plain-hadamard", np.ones(n, np.int8)))
+    x = dev(bits)
+    for label, d in ds:
+        say(f"[gpu] paley rotate n={n} m={R.outer_order(n)} {label}")
+        codes, scale, zero, y = to_np(R.rotate_quant_int4(x, torch.from_numpy(d).cuda(), y_out=True))
+        st = compare(expected(bits, d), codes, scale, zero, y, label=f"n={n} {label}")
+        say(f"[gpu] paley rotate n={n} {label}: {st}")
+
+
+@pytest.mark.parametrize("n", [12, 40, 344, 1000, 11008, 13824])
+def test_outlier_form_matches_vector_form(n):
+    """(c, sigma) against the explicit vector sigma * H[c, .] for channels in
+    the first, a middle and the last outer block, bit for bit; the first pair
+    also against the oracle."""
+    m, k = O.factor(n)
+    B = 1 << k
+    picks = [(0, 1), ((m // 2) * B + B // 3, -1), (n - 1, -1), ((m - 2) * B, 1)]
+    for i, (c, sigma) in enumerate(picks):
+        bits = W.random_rows(19, n, seed=c + 3, scale=0.8)
+        bits[:, c] = W.f32_to_bf16_bits(np.array([1100.0 * sigma], np.float32))[0]
+        d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+        say(f"[gpu] paley outlier form n={n} c={c} sigma={sigma}")
+        x = dev(bits)
+        a = to_np(R.rotate_quant_int4_outlier(x, c, sigma, y_out=True))
+        b = to_np(R.rotate_quant_int4(x, torch.from_numpy(d).cuda(), y_out=True))
+        for u, v, name in zip(a, b, ("codes", "scale", "zero", "y")):
+            assert np.array_equal(u, v), (name, c)
+        if i == 0:
+            compare(expected(bits, d), a[0], a[1], a[2], a[3], label=f"outlier n={n} c={c}")
+
+
+@pytest.mark.parametrize("n", [24, 344, 5120, 11008])
+def test_zint_matches_oracle(n):
+    g = np.random.default_rng([84, n])
+    c, sigma = int(g.integers(n)), -1
+    bits = W.random_rows(33, n, seed=c, scale=0.7, outlier=1300.0 * sigma)
+    bits[::4, c] = W.f32_to_bf16_bits(np.array([0.3], np.float32))[0]
+    d = (sigma * O.hadamard_row(n, c)).astype(np.int8)
+    say(f"[gpu] paley zint n={n} c={c}")
+    codes, scale, zero = to_np(R.rotate_quant_int4_zint(dev(bits), c, sigma))
+    y = O.rotate(O.bf16_bits_to_f64(bits), d)
+    compare_zint(y, codes, scale, zero, f"paley zint n={n}")
+
+
+@pytest.mark.parametrize("n", [40, 1000, 11008])
+def test_fold_weights_matches_oracle(n):
+    g = np.random.default_rng([42, n])
+    rows = 33
+    w_bits = W.f32_to_bf16_bits((g.standard_normal((rows, n)) / np.sqrt(n)).astype(np.float32))
+    d = O.calibrate(W.random_rows(16, n, seed=5, scale=0.7, outlier=1300.0))["d"]
+    say(f"[gpu] paley fold n={n}")
+    wf = R.fold_weights(dev(w_bits), torch.from_numpy(d).cuda()).cpu().numpy()
+    ref = O.fold_weights(w_bits, d)
+    err = np.abs(wf - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    assert err.max() <= 1e-5
+
+
+@pytest.mark.parametrize("n", [12, 344, 11008])
+def test_degenerate_rows(n):
+    c = n // 3
+    rows = np.zeros((5, n), np.uint16)
+    rows[1, :] = W.f32_to_bf16_bits(np.full(n, 2.5, np.float32))
+    rows[2, c] = W.f32_to_bf16_bits(np.array([1512.0], np.float32))[0]
+    rows[3, ::2] = 0x8000
+    rows[4] = W.random_rows(1, n, seed=3, scale=1e-3)[0]
+    d = O.calibrate(rows[2:3])["d"]
+    codes, scale, zero, y = to_np(R.rotate_quant_int4(dev(rows), torch.from_numpy(d).cuda(), y_out=True))
+    st = compare(expected(rows, d), codes, scale, zero, y, label=f"paley degenerate n={n}")
+    assert scale[0] == 1.0 and np.all(codes[0] == 0)
+    assert scale[2] == 1.0 and np.all(codes[2] == 0)  # lone outlier after the flip
+    assert st["code_mismatches"] == 0
+
+
+@pytest.mark.parametrize("t", [1, 5, 767, 769, 2053])
+def test_strided_rows_and_ragged_token_counts(t):
+    """n = 11008 with row stride n + 64 and token counts around the generic
+    kernel's grid; a seeded sample of rows (first and last included) against
+    the oracle, and on every row the extremes map to codes 0 and 15."""
+    n = 11008
+    bits = W.random_rows(t, n, seed=t, scale=0.7, outlier=1200.0)
+    d = O.calibrate(bits)["d"]
+    say(f"[gpu] paley ragged n={n} T={t}")
+    codes, scale, zero, y = to_np(R.rotate_quant_int4(dev(bits, ld=n + 64), torch.from_numpy(d).cuda(),
+                                                      y_out=True))
+    g = np.random.default_rng([12, t])
+    rows = np.unique(np.concatenate([[0, t - 1], g.choice(t, min(t, 16), replace=False)]))
+    compare(expected(bits[rows], d), codes[rows], scale[rows], zero[rows], y[rows], label=f"ragged T={t}")
+    q = O.unpack_int4(codes)
+    assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == 15)
+
+
+def test_full_size_workload_sampled():
+    """The n = 11008 workload at 8192 tokens, d from its calibration batch,
+    in the outlier form the benchmark would time: every token on the GPU,
+    a seeded sample of 32 rows (first and last included) against the oracle,
+    the vector form bit-equal on every row."""
+    name = "n11008_t8192"
+    bits, meta = W.batch(name)
+    cal = O.calibrate(W.calibration_batch(name)[0])
+    assert cal["c"] == meta["channel"]
+    say(f"[gpu] paley full size {name}")
+    x = dev(bits)
+    a = R.rotate_quant_int4_outlier(x, cal["c"], cal["sigma"])
+    b = R.rotate_quant_int4(x, torch.from_numpy(cal["d"]).cuda())
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    codes, scale, zero = to_np(a)
+    t = bits.shape[0]
+    g = np.random.default_rng(13)
+    rows = np.unique(np.concatenate([[0, t - 1], g.choice(t, 30, replace=False)]))
+    compare(expected(bits[rows], cal["d"]), codes[rows], scale[rows], zero[rows], None, label=name)
+    q = O.unpack_int4(codes)
+    assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == 15)
