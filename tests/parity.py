@@ -6,7 +6,10 @@ the method's target states:
     max(|zero|, 1);
   * int4 codes bit-exact, except a code whose exact position (y - mn)/s lies
     within 1e-4 of a rounding boundary, which may differ by +-1, on at most
-    1e-4 of the elements.
+    1e-4 of the elements.  A position exactly halfway between two levels has
+    two nearest levels, and either code is accepted there without counting
+    (the oracle takes the even one; a constant row, whose rotation is exactly
+    zero on most channels, can put thousands of outputs on one such tie).
 
 Binary32 rounds a token's largest value M by up to 2^-24 M, which in
 ordinary rows (M / s a few tens) moves a code position far less than 1e-4.
@@ -36,6 +39,7 @@ Y_TOL = 1e-5
 SZ_TOL = 1e-6
 BOUNDARY = 1e-4
 MISMATCH_FRACTION = 1e-4
+TIE = 1e-9
 U32 = 2.0 ** -24
 
 
@@ -62,7 +66,13 @@ def expected(x_bits: np.ndarray, d: np.ndarray):
     q32, _, _ = O.quant_asym(y, "f32")
     _, s, z = O.quant_asym(y, "f64")
     pos = O.code_position(y, "f32")
-    return {"y": y, "q": q32, "scale": s, "zero": z, "pos": pos}
+    return {"y": y, "q": q32, "scale": s, "zero": z, "pos": pos, "pos64": O.code_position(y, "f64")}
+
+
+def exact_tie(pos64: np.ndarray) -> np.ndarray:
+    """Positions that are exactly halfway between two levels (within binary64
+    rounding): both neighbours are nearest levels, so either code is right."""
+    return np.abs(pos64 - np.floor(pos64) - 0.5) < TIE
 
 
 def compare(exp: dict, codes_packed: np.ndarray, scale: np.ndarray, zero: np.ndarray,
@@ -95,7 +105,11 @@ def compare(exp: dict, codes_packed: np.ndarray, scale: np.ndarray, zero: np.nda
         win = np.broadcast_to(position_window(y, exp["scale"])[:, None], q.shape)[bad]
         assert np.all(np.abs(diff[bad]) == 1), f"{label}: a code differs by more than 1"
         assert np.all(dist < win), f"{label}: code mismatch {dist.max():.3e} away from a boundary"
-        # "at most 1e-4 of the elements", counted in whole elements (rounded up)
-        near = int((dist < BOUNDARY).sum())
+        # "at most 1e-4 of the elements", counted in whole elements (rounded
+        # up); exact ties (either neighbour is a nearest level) do not count
+        ties = exact_tie(exp["pos64"][bad])
+        stats["tie_mismatches"] = int(ties.sum())
+        stats["code_mismatches"] = nbad - stats["tie_mismatches"]
+        near = int(((dist < BOUNDARY) & ~ties).sum())
         assert near <= math.ceil(MISMATCH_FRACTION * q.size), f"{label}: {near} mismatches of {q.size}"
     return stats
