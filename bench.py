@@ -42,19 +42,23 @@ WORKLOAD = "n14336_t8192"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # Sources that define the timed kernel; the HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
-KERNEL_SOURCES = ("rotation_activation_quantization_amd/csrc/rq_fast.hip",
-                  "rotation_activation_quantization_amd/csrc/wave_ops.h",
-                  "rotation_activation_quantization_amd/csrc/device_common.h",
-                  "rotation_activation_quantization_amd/csrc/internal.h",
+_CSRC = "rotation_activation_quantization_amd/csrc/"
+KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h", _CSRC + "internal.h",
                   "rotation_activation_quantization_amd/build.py")
+GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h",
+                   "rotation_activation_quantization_amd/build.py")
 TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"
 
 
-def kernel_source_digest() -> str:
+def kernel_sources(kernel: str):
+    return GENERIC_SOURCES if kernel == "rq_generic" else KERNEL_SOURCES
+
+
+def kernel_source_digest(kernel: str = "") -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in kernel_sources(kernel):
         with open(os.path.join(HERE, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -73,7 +77,7 @@ def measured_traffic(kernel: str, n: int, t: int):
             if "=" in ln and not ln.startswith("#"):
                 k, v = ln.strip().split("=", 1)
                 kv[k] = v
-    if kv.get("source_sha256") != kernel_source_digest():
+    if kv.get("source_sha256") != kernel_source_digest(kernel):
         return None
     return float(kv["traffic_bytes_per_launch"])
 
@@ -305,7 +309,8 @@ def torch_int16():
 
 def workload_text(w, n: int, t: int, c: int) -> str:
     width = {4096: "2^12", 8192: "2^13", 14336: "28*2^9, LLaMA3-8B down_proj input",
-             28672: "28*2^10, LLaMA3-70B down_proj input"}.get(n, str(n))
+             28672: "28*2^10, LLaMA3-70B down_proj input",
+             11008: "344*2^5, Paley I over GF(7^3), LLaMA-2-7B down_proj input"}.get(n, str(n))
     law = f"N(0,{w.width:g})" if w.law == "normal" else f"{w.width:g}*t({w.df:g})"
     sign = "+" if w.p_positive >= 1.0 else f"+-(+ {w.p_positive:.0%})"
     mild = f", {w.mild_channels} mild channels x{w.mild_factor:g}" if w.mild_channels else ""
@@ -389,7 +394,9 @@ def main() -> int:
     ap.add_argument("--linear", action="store_true",
                     help="time the INT4-activation down-projection signrot_int4_linear instead "
                          "(8192 x 14336 codes, W' 4096 x 14336 bf16)")
-    ap.add_argument("--workload", default=WORKLOAD, choices=["n4096_t64", "n8192_t2048", "n14336_t4096", "n14336_t8192", "n28672_t8192"],
+    ap.add_argument("--workload", default=WORKLOAD,
+                    choices=["n4096_t64", "n8192_t2048", "n14336_t4096", "n14336_t8192", "n28672_t8192",
+                             "n11008_t8192"],
                     help="synthetic workload to time (default: n=14336 x 8192 tokens)")
     args = ap.parse_args()
     if args.gpus != 1:

@@ -19,6 +19,7 @@ SOURCES = [
     "api.hip",
     "rq_generic.hip",
     "rq_fast.hip",
+    "rq_outer.hip",
     "calib_dequant.hip",
     "linear.hip",
     "hadamard28.cpp",

@@ -64,7 +64,7 @@ Shape factor_n(int64_t n) {
   return s;
 }
 
-const uint32_t* outer_mask_device(int m, hipError_t* err) {
+const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed) {
   *err = hipSuccess;
   static std::mutex mu;
   static std::vector<std::vector<std::pair<int, uint32_t*>>> per_dev;
@@ -72,18 +72,26 @@ const uint32_t* outer_mask_device(int m, hipError_t* err) {
   if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
   if (dev >= static_cast<int>(per_dev.size())) per_dev.resize(dev + 1);
+  const int key = transposed ? -m : m;
   for (auto& e : per_dev[dev])
-    if (e.first == m) return e.second;
+    if (e.first == key) return e.second;
   std::vector<uint32_t> mask;
   if (m == 28) {  // h28(): one word per row
-    mask.assign(h28().rowmask, h28().rowmask + 28);
+    if (transposed) {
+      mask.assign(28, 0u);
+      for (int r = 0; r < 28; ++r)
+        for (int c = 0; c < 28; ++c)
+          if (h28().h[r][c] < 0) mask[c] |= 1u << r;
+    } else {
+      mask.assign(h28().rowmask, h28().rowmask + 28);
+    }
   } else {
     const OuterTable* t = outer_table(m);
     if (!t) {
       *err = hipErrorInvalidValue;
       return nullptr;
     }
-    mask = t->mask;
+    mask = transposed ? t->mask_t : t->mask;
   }
   uint32_t* ptr = nullptr;
   if ((*err = hipMalloc(&ptr, mask.size() * sizeof(uint32_t))) != hipSuccess) return nullptr;
@@ -91,8 +99,40 @@ const uint32_t* outer_mask_device(int m, hipError_t* err) {
     (void)hipFree(ptr);
     return nullptr;
   }
-  per_dev[dev].push_back({m, ptr});
+  per_dev[dev].push_back({key, ptr});
   return ptr;
+}
+
+// The rotate kernel for a shape: the 28 * 2^k / 2^k MFMA kernels, the
+// outer-order MFMA kernel, or the generic one.
+enum class RqKernel { kFast, kOuter, kGeneric };
+
+RqKernel rq_kernel_for(const Shape& sh) {
+  if (rq_fast_supports(sh.n, sh.k, sh.m28)) return RqKernel::kFast;
+  if (rq_outer_supports(sh.m, sh.k)) return RqKernel::kOuter;
+  return RqKernel::kGeneric;
+}
+
+// Fills the outer-factor fields of a (the device sign tables it needs).
+hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
+  hipError_t he = hipSuccess;
+  a.m = sh.m;
+  a.hw = (sh.m + 31) / 32;
+  a.hm = nullptr;
+  a.hmt = nullptr;
+  if (sh.m > 1) {
+    if (!(a.hm = outer_mask_device(sh.m, &he))) return he;
+    if (rq_kernel_for(sh) == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, true))) return he;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_rq(const RqArgs& a, const Shape& sh, hipStream_t s) {
+  switch (rq_kernel_for(sh)) {
+    case RqKernel::kFast: return launch_rq_fast(a, s);
+    case RqKernel::kOuter: return launch_rq_outer(a, s);
+    default: return launch_rq_generic(a, s);
+  }
 }
 
 int device_cu_count() {
@@ -161,7 +201,11 @@ int signrot_debug_outer(int m, int8_t* out) {
 const char* signrot_kernel_name(int64_t n) {
   const Shape sh = factor_n(n);
   if (!sh.ok) return nullptr;
-  return rq_fast_supports(sh.n, sh.k, sh.m28) ? rq_fast_name(sh.n) : rq_generic_name();
+  switch (rq_kernel_for(sh)) {
+    case RqKernel::kFast: return rq_fast_name(sh.n);
+    case RqKernel::kOuter: return rq_outer_name();
+    default: return rq_generic_name();
+  }
 }
 
 int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
@@ -235,14 +279,11 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    hipError_t he = hipSuccess;
-    a.m = sh.m;
-    a.hw = (sh.m + 31) / 32;
-    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
-    if (sh.m > 1 && !a.hm) return fail_hip(he, "outer Hadamard factor table");
+    const hipError_t he = set_outer_tables(a, sh);
+    if (he != hipSuccess) return fail_hip(he, "outer Hadamard factor table");
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, st) : launch_rq_generic(a, st);
+  hipError_t e = launch_rq(a, sh, st);
   if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4 launch");
   return SIGNROT_OK;
 }
@@ -289,15 +330,12 @@ int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int
   a.zint = zint;
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    hipError_t he = hipSuccess;
-    a.m = sh.m;
-    a.hw = (sh.m + 31) / 32;
-    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
-    if (sh.m > 1 && !a.hm) return fail_hip(he, "outer Hadamard factor table");
+    const hipError_t he = set_outer_tables(a, sh);
+    if (he != hipSuccess) return fail_hip(he, "outer Hadamard factor table");
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  if (rq_fast_supports(sh.n, sh.k, sh.m28)) {
-    const hipError_t e = launch_rq_fast(a, st);
+  if (rq_kernel_for(sh) != RqKernel::kGeneric) {
+    const hipError_t e = launch_rq(a, sh, st);
     if (e != hipSuccess) return fail_hip(e, "rotate_quant_int4_outlier launch");
     return SIGNROT_OK;
   }
@@ -370,16 +408,13 @@ int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    hipError_t he = hipSuccess;
-    a.m = sh.m;
-    a.hw = (sh.m + 31) / 32;
-    a.hm = sh.m > 1 ? outer_mask_device(sh.m, &he) : nullptr;
-    if (sh.m > 1 && !a.hm) {
+    const hipError_t he = set_outer_tables(a, sh);
+    if (he != hipSuccess) {
       (void)hipFreeAsync(scratch, s);
       return fail_hip(he, "outer Hadamard factor table");
     }
   }
-  e = rq_fast_supports(sh.n, sh.k, sh.m28) ? launch_rq_fast(a, s) : launch_rq_generic(a, s);
+  e = launch_rq(a, sh, s);
   const hipError_t ef = hipFreeAsync(scratch, s);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return fail_hip(e, "fold_weights launch");

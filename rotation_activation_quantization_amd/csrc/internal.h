@@ -24,19 +24,21 @@ Shape factor_n(int64_t n);
 // Outer factors other than order 28's hand-built table: Paley's
 // constructions I and II (outer.cpp).  outer_order_for returns m or 0;
 // outer_table returns the cached host table (nullptr when no construction);
-// mask[r * words + w] has bit b set iff H_m[r][32 w + b] == -1.
+// mask[r * words + w] has bit b set iff H_m[r][32 w + b] == -1; mask_t is
+// the same for the transpose (mask_t[r * words + w] bit b: H_m[32 w + b][r]).
 struct OuterTable {
   int m = 0;
   int words = 0;
   std::vector<int8_t> h;  // m x m, row-major
   std::vector<uint32_t> mask;
+  std::vector<uint32_t> mask_t;
 };
 int outer_order_for(int odd, int v);
 const OuterTable* outer_table(int m);
 // The mask table of H_m on the current device: copied there on first use
 // (hipMalloc + hipMemcpy, not capturable) and kept until the process ends.
-// nullptr (with *err set) on failure.
-const uint32_t* outer_mask_device(int m, hipError_t* err);
+// nullptr (with *err set) on failure.  transposed: the table of H_m^T.
+const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed = false);
 
 // The library's order-28 Hadamard matrix (Paley construction I over GF(27)),
 // built once on the host.  rowmask[a] has bit a' set iff H28[a][a'] == -1.
@@ -75,6 +77,7 @@ struct RqArgs {
   int m;                 // outer order (1: none)
   int hw;                // 32-bit words per mask row of H_m
   const uint32_t* hm;    // device mask table of H_m (m > 1), see OuterTable
+  const uint32_t* hmt;   // device mask table of H_m^T (set for the outer-order MFMA kernel)
 };
 
 // Launchers; each returns the hipError_t of the launch.
@@ -83,6 +86,11 @@ const char* rq_generic_name();
 bool rq_fast_supports(int n, int k, bool m28);
 hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s);
 const char* rq_fast_name(int n);
+// MFMA kernel for outer Paley orders m != 28 with 32 <= 2^k <= 256 (shapes in
+// its table); rq_outer_supports is host-only.
+bool rq_outer_supports(int m, int k);
+hipError_t launch_rq_outer(const RqArgs& a, hipStream_t s);
+const char* rq_outer_name();
 
 hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
                             int8_t* d_out, unsigned long long* scratch, hipStream_t s);

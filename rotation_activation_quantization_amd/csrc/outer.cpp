@@ -192,6 +192,10 @@ bool build(int m, OuterTable* out) {
   for (int i = 0; i < m; ++i)
     for (int j = 0; j < m; ++j)
       if (out->h[static_cast<size_t>(i) * m + j] < 0) out->mask[static_cast<size_t>(i) * out->words + j / 32] |= 1u << (j % 32);
+  out->mask_t.assign(static_cast<size_t>(m) * out->words, 0u);
+  for (int i = 0; i < m; ++i)
+    for (int j = 0; j < m; ++j)
+      if (out->h[static_cast<size_t>(i) * m + j] < 0) out->mask_t[static_cast<size_t>(j) * out->words + i / 32] |= 1u << (i % 32);
   return true;
 }
 

@@ -340,6 +340,9 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       rd[w] = mn;
       rd[16 + w] = mx;
     }
+    // x_c of this row, read before the barrier: the previous barrier published
+    // it, and its slot is next written (for the row after next) after this one
+    const float xc = GENERAL ? 0.0f : xcl[par];
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < S::kWaves; q += 4) {
@@ -359,7 +362,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 
     // (5) quantize, pack, store
     const QuantParams qp = quant_params(mn, mx);
-    const float shift = GENERAL ? 0.0f : (sig > 0 ? xcl[par] : -xcl[par]);
+    const float shift = sig > 0 ? xc : -xc;
     // code of value v: rne(v * inv + cq); with the integer zero-point z the
     // code is rne((v + shift) * inv + z), so cq = shift * inv + z
     float cq = qp.cq;

@@ -1,8 +1,10 @@
 """Parity of the HIP path with the oracle at widths n = m * 2^k whose outer
 factor H_m is a Paley matrix of an order other than 28 (Paley I for
 m - 1 = 11, 19, 43, 107, 139, 343, ...; Paley II for m / 2 - 1 = 5, 9, 13,
-49, 73, ...).  These shapes run the generic kernel; the oracle builds H_m by
-its own finite-field arithmetic (numpy), the library by its own (C++).
+49, 73, ...).  Widths with 32 <= n / m <= 256 in the outer-order MFMA
+kernel's table run it (every instantiated shape appears below); the others
+run the generic kernel.  The oracle builds H_m by its own finite-field
+arithmetic (numpy), the library by its own (C++).
 
 Tolerances are the ones in parity.py (rotated values within 1e-5 of the
 token's max |y|, scale and zero-point within 1e-6, codes bit-exact except at
@@ -26,8 +28,11 @@ pytestmark = pytest.mark.gpu
 
 # (n, (m, k)): small orders that still span several outer blocks, and the
 # MLP widths of common models (11008, 13824, 18944) plus two-factor widths
-WIDTHS = [12, 20, 24, 40, 72, 344, 1000, 5120, 8960, 11008, 13824, 18944, 24576]
+WIDTHS = [12, 20, 24, 40, 72, 344, 1000, 2560, 4864, 5120, 5632, 8960, 11008, 13824, 17408, 18944, 24576, 27648]
 CHEAP = [n for n in WIDTHS if n <= 8960]
+# the kernel each width runs: (K chunks, column tiles) of the MFMA kernel's table
+OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5120: (1, 16), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
+              13824: (4, 8), 17408: (3, 16), 18944: (5, 8), 27648: (4, 16)}
 
 
 def say(msg):
@@ -47,11 +52,15 @@ def to_np(outs):
     return [o.cpu().numpy() if o is not None else None for o in outs]
 
 
-def test_widths_use_the_intended_outer_orders():
+def test_widths_use_the_intended_outer_orders_and_kernels():
     for n in WIDTHS:
         m, k = O.factor(n)
         assert m not in (1, 28) and R.outer_order(n) == m, n
-        assert R.kernel_name(n) == "rq_generic", n
+        if n in OUTER_MFMA:
+            assert OUTER_MFMA[n] == ((m + 31) // 32, (1 << k) // 16), n
+            assert R.kernel_name(n) == "rq_outer_mfma", n
+        else:
+            assert R.kernel_name(n) == "rq_generic", n
 
 
 @pytest.mark.parametrize("n", WIDTHS)
@@ -89,7 +98,7 @@ def test_rotate_quant_matches_oracle(n):
         say(f"[gpu] paley rotate n={n} {label}: {st}")
 
 
-@pytest.mark.parametrize("n", [12, 40, 344, 1000, 11008, 13824])
+@pytest.mark.parametrize("n", [12, 40, 344, 1000, 2560, 4864, 5120, 5632, 8960, 11008, 13824, 17408, 18944, 27648])
 def test_outlier_form_matches_vector_form(n):
     """(c, sigma) against the explicit vector sigma * H[c, .] for channels in
     the first, a middle and the last outer block, bit for bit; the first pair
@@ -111,7 +120,7 @@ def test_outlier_form_matches_vector_form(n):
             compare(expected(bits, d), a[0], a[1], a[2], a[3], label=f"outlier n={n} c={c}")
 
 
-@pytest.mark.parametrize("n", [24, 344, 5120, 11008])
+@pytest.mark.parametrize("n", [24, 344, 2560, 4864, 5120, 5632, 8960, 11008, 13824, 17408, 18944, 27648])
 def test_zint_matches_oracle(n):
     g = np.random.default_rng([84, n])
     c, sigma = int(g.integers(n)), -1
@@ -124,7 +133,7 @@ def test_zint_matches_oracle(n):
     compare_zint(y, codes, scale, zero, f"paley zint n={n}")
 
 
-@pytest.mark.parametrize("n", [40, 1000, 11008])
+@pytest.mark.parametrize("n", [40, 1000, 5120, 11008, 13824])
 def test_fold_weights_matches_oracle(n):
     g = np.random.default_rng([42, n])
     rows = 33
@@ -137,7 +146,7 @@ def test_fold_weights_matches_oracle(n):
     assert err.max() <= 1e-5
 
 
-@pytest.mark.parametrize("n", [12, 344, 11008])
+@pytest.mark.parametrize("n", [12, 344, 5120, 11008, 13824, 27648])
 def test_degenerate_rows(n):
     c = n // 3
     rows = np.zeros((5, n), np.uint16)
@@ -153,18 +162,19 @@ def test_degenerate_rows(n):
     assert st["code_mismatches"] == 0
 
 
-@pytest.mark.parametrize("t", [1, 5, 767, 769, 2053])
-def test_strided_rows_and_ragged_token_counts(t):
-    """n = 11008 with row stride n + 64 and token counts around the generic
-    kernel's grid; a seeded sample of rows (first and last included) against
-    the oracle, and on every row the extremes map to codes 0 and 15."""
-    n = 11008
+@pytest.mark.parametrize("n,t", [(11008, 1), (11008, 5), (11008, 255), (11008, 257), (11008, 769), (11008, 2053),
+                                 (13824, 511), (13824, 513), (27648, 255), (27648, 257), (5120, 1025)])
+def test_strided_rows_and_ragged_token_counts(n, t):
+    """Row stride n + 64 and token counts around the launch grid (one or
+    several rows per work-group, fewer rows than work-groups); a seeded
+    sample of rows (first and last included) against the oracle, and on every
+    row the extremes map to codes 0 and 15."""
     bits = W.random_rows(t, n, seed=t, scale=0.7, outlier=1200.0)
     d = O.calibrate(bits)["d"]
     say(f"[gpu] paley ragged n={n} T={t}")
     codes, scale, zero, y = to_np(R.rotate_quant_int4(dev(bits, ld=n + 64), torch.from_numpy(d).cuda(),
                                                       y_out=True))
-    g = np.random.default_rng([12, t])
+    g = np.random.default_rng([12, n, t])
     rows = np.unique(np.concatenate([[0, t - 1], g.choice(t, min(t, 16), replace=False)]))
     compare(expected(bits[rows], d), codes[rows], scale[rows], zero[rows], y[rows], label=f"ragged T={t}")
     q = O.unpack_int4(codes)
@@ -173,9 +183,9 @@ def test_strided_rows_and_ragged_token_counts(t):
 
 def test_full_size_workload_sampled():
     """The n = 11008 workload at 8192 tokens, d from its calibration batch,
-    in the outlier form the benchmark would time: every token on the GPU,
-    a seeded sample of 32 rows (first and last included) against the oracle,
-    the vector form bit-equal on every row."""
+    in the outlier form the benchmark times: every token on the GPU, a seeded
+    sample of 32 rows (first and last included) against the oracle, the
+    vector form bit-equal on every row."""
     name = "n11008_t8192"
     bits, meta = W.batch(name)
     cal = O.calibrate(W.calibration_batch(name)[0])
