@@ -47,11 +47,13 @@ KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_c
                   "rotation_activation_quantization_amd/build.py")
 GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h",
                    "rotation_activation_quantization_amd/build.py")
+OUTER_SOURCES = (_CSRC + "rq_outer.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h", _CSRC + "internal.h",
+                 "rotation_activation_quantization_amd/build.py")
 TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"
 
 
 def kernel_sources(kernel: str):
-    return GENERIC_SOURCES if kernel == "rq_generic" else KERNEL_SOURCES
+    return {"rq_generic": GENERIC_SOURCES, "rq_outer_mfma": OUTER_SOURCES}.get(kernel, KERNEL_SOURCES)
 
 
 def kernel_source_digest(kernel: str = "") -> str:
