@@ -44,6 +44,8 @@
 // min / max.
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "wave_ops.h"
 
@@ -464,7 +466,9 @@ template <int KA, int KB>
 hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
   using S = FastShape<KA, KB>;
   // resident workgroups per CU (registers and LDS), asked once per shape
-  static int per_cu = 0;
+  // (computed by any thread that finds 0; all compute the same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, rq_fast_kernel<KA, KB, false>, S::kThreads, 0) !=
@@ -472,6 +476,7 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
         blocks < 1)
       blocks = 1;
     per_cu = blocks;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
   if (grid > a.tokens) grid = a.tokens;

@@ -40,6 +40,8 @@
 // as a sign-bit XOR after stage 2.
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "wave_ops.h"
 
@@ -302,9 +304,17 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
       rd[16 + w] = mx;
     }
     lds_barrier();
-    for (int q = 0; q < nw; ++q) {
-      mn = fmin_raw(mn, rd[q]);
-      mx = fmax_raw(mx, rd[16 + q]);
+    // the other waves' min / max, four per 16-byte read
+    for (int q = 0; q < nw; q += 4) {
+      const f32x4_t m4 = *reinterpret_cast<const f32x4_t*>(rd + q);
+      const f32x4_t x4 = *reinterpret_cast<const f32x4_t*>(rd + 16 + q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (q + k < nw) {
+          mn = fmin_raw(mn, m4[k]);
+          mx = fmax_raw(mx, x4[k]);
+        }
+      }
     }
 
     // (5) quantize, pack, store
@@ -399,17 +409,20 @@ hipError_t launch_outer_shape(const RqArgs& a, hipStream_t stream) {
   const int waves = ((a.m + 15) / 16 + MTW - 1) / MTW;
   const int threads = 64 * waves;
   // resident work-groups per CU at this block size, asked once per size
-  static int per_cu[17] = {0};
-  if (per_cu[waves] == 0) {
+  // (computed by any thread that finds 0; all compute the same value)
+  static std::atomic<int> per_cu_cache[17];
+  int per_cu = per_cu_cache[waves].load(std::memory_order_relaxed);
+  if (per_cu == 0) {
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &blocks, reinterpret_cast<const void*>(&rq_outer_kernel<KC, NTL, MTW, false, false>), threads, 0) !=
             hipSuccess ||
         blocks < 1)
       blocks = 1;
-    per_cu[waves] = blocks;
+    per_cu = blocks;
+    per_cu_cache[waves].store(per_cu, std::memory_order_relaxed);
   }
-  int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu[waves];
+  int64_t grid = static_cast<int64_t>(device_cu_count()) * per_cu;
   if (grid > a.tokens) grid = a.tokens;
   const dim3 blocks(static_cast<unsigned>(grid));
   const dim3 thr(static_cast<unsigned>(threads));
