@@ -267,3 +267,44 @@ def test_header_is_plain_c(tmp_path):
     r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-fsyntax-only",
                         "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+# (K chunks, column tiles) -> M-tiles per wave of the outer-order MFMA kernel
+OUTER_TABLE = {(11, 2): 2, (4, 8): 1, (5, 8): 1, (5, 4): 1, (4, 16): 1, (3, 4): 1, (3, 16): 1, (2, 8): 1,
+               (1, 16): 1, (1, 8): 1}
+
+
+def _expected_kernel(n):
+    """The dispatch rule restated: the 2^k and 28 * 2^k MFMA kernels for their
+    widths; the outer-order kernel for other Paley orders with 32 <= 2^k <= 256
+    whose (K chunks, column tiles) is in its table and whose work-group fits 16
+    waves with a staging unit per thread; the generic kernel otherwise."""
+    m, k = O.factor(n)
+    if n in (4096, 8192, 16384):
+        return "rq_mfma32_w8"
+    if m == 28 and k in (7, 8, 9):
+        return "rq_mfma28_w7"
+    if n == 28672:
+        return "rq_mfma56_w14"
+    if m > 1 and m != 28 and 5 <= k <= 8:
+        kc, ntl = (m + 31) // 32, 1 << (k - 4)
+        mtw = OUTER_TABLE.get((kc, ntl))
+        if mtw:
+            waves = -(-(-(-m // 16)) // mtw)
+            if waves <= 16 and m * ntl <= 64 * waves * ((ntl * mtw + 3) // 4):
+                return "rq_outer_mfma"
+    return "rq_generic"
+
+
+def test_kernel_dispatch_rule():
+    """Host-only: the kernel the library picks for every supported n up to
+    32768 (in steps of 4) equals the rule above."""
+    seen = set()
+    for n in [2] + list(range(4, 32769, 4)):
+        if not R.supported_n(n):
+            continue
+        want = _expected_kernel(n)
+        assert R.kernel_name(n) == want, (n, R.kernel_name(n), want)
+        seen.add(want)
+    assert seen == {"rq_mfma32_w8", "rq_mfma28_w7", "rq_mfma56_w14", "rq_outer_mfma", "rq_generic"}
+
