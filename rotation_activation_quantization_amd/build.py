@@ -20,6 +20,10 @@ SOURCES = [
     "rq_generic.hip",
     "rq_fast.hip",
     "rq_outer.hip",
+    "rq_outer_t2.hip",
+    "rq_outer_t4.hip",
+    "rq_outer_t8.hip",
+    "rq_outer_t16.hip",
     "calib_dequant.hip",
     "linear.hip",
     "hadamard28.cpp",

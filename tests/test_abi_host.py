@@ -270,8 +270,9 @@ def test_header_is_plain_c(tmp_path):
 
 
 # (K chunks, column tiles) -> M-tiles per wave of the outer-order MFMA kernel
-OUTER_TABLE = {(11, 2): 2, (4, 8): 1, (5, 8): 1, (5, 4): 1, (4, 16): 1, (3, 4): 1, (3, 16): 1, (2, 8): 1,
-               (1, 16): 1, (1, 8): 1}
+OUTER_TABLE = {**{(kc, 2): 1 for kc in range(1, 9)}, **{(kc, 2): 2 for kc in range(9, 13)},
+               **{(kc, 4): 1 for kc in range(1, 9)}, **{(kc, 8): 1 for kc in range(1, 7)},
+               **{(kc, 16): 1 for kc in range(1, 5)}}
 
 
 def _expected_kernel(n):

@@ -4,7 +4,8 @@ m - 1 = 11, 19, 43, 107, 139, 343, ...; Paley II for m / 2 - 1 = 5, 9, 13,
 49, 73, ...).  Widths with 32 <= n / m <= 256 in the outer-order MFMA
 kernel's table run it (every instantiated shape appears below); the others
 run the generic kernel.  The oracle builds H_m by its own finite-field
-arithmetic (numpy), the library by its own (C++).
+arithmetic (numpy), the library by its own (C++).  The last test takes one
+width for each remaining shape of the MFMA kernel's table.
 
 Tolerances are the ones in parity.py (rotated values within 1e-5 of the
 token's max |y|, scale and zero-point within 1e-6, codes bit-exact except at
@@ -204,3 +205,41 @@ def test_full_size_workload_sampled():
     compare(expected(bits[rows], cal["d"]), codes[rows], scale[rows], zero[rows], None, label=name)
     q = O.unpack_int4(codes)
     assert np.all(q.min(axis=1) == 0) and np.all(q.max(axis=1) == 15)
+
+
+# one width per shape of the MFMA kernel's table not covered above:
+# (K chunks, column tiles) -> n
+MORE_SHAPES = {(1, 2): 384, (1, 4): 768, (1, 16): 3072, (2, 2): 1152, (2, 4): 2304, (2, 16): 9216, (3, 2): 2176,
+               (3, 8): 8704, (4, 2): 3200, (4, 4): 6400, (5, 2): 4224, (6, 2): 5248, (6, 4): 10496, (6, 8): 20992,
+               (7, 2): 6272, (7, 4): 12544, (8, 2): 7296, (8, 4): 14592, (9, 2): 8832, (10, 2): 9600, (12, 2): 11648}
+
+
+@pytest.mark.parametrize("n", sorted(MORE_SHAPES.values()))
+def test_every_mfma_shape_matches_oracle(n):
+    """For each remaining shape: the calibrated sign vector and a random one
+    through the d-vector entry point against the oracle, the outlier form
+    bit-equal to the vector form, and the integer zero-point form against the
+    oracle."""
+    m, k = O.factor(n)
+    assert MORE_SHAPES[((m + 31) // 32, (1 << k) // 16)] == n
+    assert R.kernel_name(n) == "rq_outer_mfma"
+    t = 19
+    bits = W.random_rows(t, n, seed=n + 7, scale=0.8)
+    c = (n * 5) // 13
+    bits[::2, c] = W.f32_to_bf16_bits(np.array([-1000.0], np.float32))[0]
+    cal = O.calibrate(bits)
+    assert cal["c"] == c
+    g = np.random.default_rng([17, n])
+    rnd = np.where(g.random(n) < 0.5, -1, 1).astype(np.int8)
+    x = dev(bits)
+    for label, d in (("signrot-d", cal["d"]), ("random-d", rnd)):
+        say(f"[gpu] shape n={n} m={m} {label}")
+        codes, scale, zero, y = to_np(R.rotate_quant_int4(x, torch.from_numpy(d).cuda(), y_out=True))
+        compare(expected(bits, d), codes, scale, zero, y, label=f"n={n} {label}")
+    a = to_np(R.rotate_quant_int4_outlier(x, cal["c"], cal["sigma"], y_out=True))
+    b = to_np(R.rotate_quant_int4(x, torch.from_numpy(cal["d"]).cuda(), y_out=True))
+    for u, v, name in zip(a, b, ("codes", "scale", "zero", "y")):
+        assert np.array_equal(u, v), name
+    codes, scale, zero = to_np(R.rotate_quant_int4_zint(x, cal["c"], cal["sigma"]))
+    compare_zint(O.rotate(O.bf16_bits_to_f64(bits), cal["d"]), codes, scale, zero, f"zint n={n}")
+
