@@ -64,7 +64,7 @@ Shape factor_n(int64_t n) {
   return s;
 }
 
-const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed) {
+const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed, int fold) {
   *err = hipSuccess;
   static std::mutex mu;
   static std::vector<std::vector<std::pair<int, uint32_t*>>> per_dev;
@@ -72,11 +72,18 @@ const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed) {
   if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
   std::lock_guard<std::mutex> lock(mu);
   if (dev >= static_cast<int>(per_dev.size())) per_dev.resize(dev + 1);
-  const int key = transposed ? -m : m;
+  const int key = ((m * 16 + fold) * 2) + (transposed ? 1 : 0);
   for (auto& e : per_dev[dev])
     if (e.first == key) return e.second;
   std::vector<uint32_t> mask;
-  if (m == 28) {  // h28(): one word per row
+  if (fold > 0) {
+    const OuterTable* t = outer_table_folded(m, fold);
+    if (!t) {
+      *err = hipErrorInvalidValue;
+      return nullptr;
+    }
+    mask = transposed ? t->mask_t : t->mask;
+  } else if (m == 28) {  // h28(): one word per row
     if (transposed) {
       mask.assign(28, 0u);
       for (int r = 0; r < 28; ++r)
@@ -104,25 +111,46 @@ const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed) {
 }
 
 // The rotate kernel for a shape: the 28 * 2^k / 2^k MFMA kernels, the
-// outer-order MFMA kernel, or the generic one.
+// outer-order MFMA kernel, or the generic one.  The outer-order kernel also
+// takes n = m 2^k read as (m 2^fold) 2^(k - fold): the same H with fold
+// Sylvester index bits moved into its outer factor, for 2^k beyond its
+// table (2^k > 256) or a Sylvester width without a fast kernel.
 enum class RqKernel { kFast, kOuter, kGeneric };
+struct RqPlan {
+  RqKernel kind;
+  int fold;
+};
 
-RqKernel rq_kernel_for(const Shape& sh) {
-  if (rq_fast_supports(sh.n, sh.k, sh.m28)) return RqKernel::kFast;
-  if (rq_outer_supports(sh.m, sh.k)) return RqKernel::kOuter;
-  return RqKernel::kGeneric;
+RqPlan rq_plan_for(const Shape& sh) {
+  if (rq_fast_supports(sh.n, sh.k, sh.m28)) return {RqKernel::kFast, 0};
+  if (rq_outer_supports(sh.m, sh.k)) return {RqKernel::kOuter, 0};
+  if (sh.m == 1 || (sh.m != 28 && sh.k > 8)) {
+    // 2^(k - fold) = 128 first (the kernel's best column-tile count), then 256, 32, 64
+    for (const int kk : {7, 8, 5, 6}) {
+      const int fold = sh.k - kk;
+      const int64_t mm = static_cast<int64_t>(sh.m) << (fold > 0 ? fold : 0);
+      if (fold >= (sh.m == 1 ? 2 : 1) && mm <= kMaxOuter && rq_outer_supports(static_cast<int>(mm), kk))
+        return {RqKernel::kOuter, fold};
+    }
+  }
+  return {RqKernel::kGeneric, 0};
 }
 
-// Fills the outer-factor fields of a (the device sign tables it needs).
+RqKernel rq_kernel_for(const Shape& sh) { return rq_plan_for(sh).kind; }
+
+// Fills the outer-factor fields of a (the device sign tables it needs); with
+// a fold, also the outer order and Sylvester exponent the kernel sees.
 hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
   hipError_t he = hipSuccess;
-  a.m = sh.m;
-  a.hw = (sh.m + 31) / 32;
+  const RqPlan p = rq_plan_for(sh);
+  a.m = sh.m << p.fold;
+  a.k = sh.k - p.fold;
+  a.hw = (a.m + 31) / 32;
   a.hm = nullptr;
   a.hmt = nullptr;
-  if (sh.m > 1) {
-    if (!(a.hm = outer_mask_device(sh.m, &he))) return he;
-    if (rq_kernel_for(sh) == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, true))) return he;
+  if (a.m > 1) {
+    if (!(a.hm = outer_mask_device(sh.m, &he, false, p.fold))) return he;
+    if (p.kind == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, true, p.fold))) return he;
   }
   return hipSuccess;
 }

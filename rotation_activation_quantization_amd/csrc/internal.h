@@ -35,10 +35,15 @@ struct OuterTable {
 };
 int outer_order_for(int odd, int v);
 const OuterTable* outer_table(int m);
+// H_m (x) Syl_{2^j} as one outer factor of order m 2^j <= kMaxOuter (m = 1:
+// the Sylvester matrix; m = 28: the order-28 table; else Paley): the same H
+// read with j Sylvester index bits moved into the outer index.
+const OuterTable* outer_table_folded(int m, int j);
 // The mask table of H_m on the current device: copied there on first use
 // (hipMalloc + hipMemcpy, not capturable) and kept until the process ends.
-// nullptr (with *err set) on failure.  transposed: the table of H_m^T.
-const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed = false);
+// nullptr (with *err set) on failure.  transposed: the table of H_m^T;
+// fold: of H_m (x) Syl_{2^fold} (outer_table_folded).
+const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed = false, int fold = 0);
 
 // The library's order-28 Hadamard matrix (Paley construction I over GF(27)),
 // built once on the host.  rowmask[a] has bit a' set iff H28[a][a'] == -1.

@@ -222,4 +222,46 @@ const OuterTable* outer_table(int m) {
   return &cache.emplace(m, std::move(t)).first->second;
 }
 
+const OuterTable* outer_table_folded(int m, int j) {
+  if (j == 0 && m > 1 && m != 28) return outer_table(m);
+  const int64_t mm = static_cast<int64_t>(m) << j;
+  if (m < 1 || j < 0 || mm > kMaxOuter || mm < 2) return nullptr;
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, OuterTable> cache;
+  // the factor H_m: Sylvester's [[1]] for m = 1, the order-28 table, or Paley
+  std::vector<int8_t> base;
+  if (m == 1) {
+    base.assign(1, 1);
+  } else if (m == 28) {
+    base.assign(&h28().h[0][0], &h28().h[0][0] + 28 * 28);
+  } else {
+    const OuterTable* t = outer_table(m);
+    if (!t) return nullptr;
+    base = t->h;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({m, j});
+  if (it != cache.end()) return &it->second;
+  // H_m (x) Syl_{2^j}: entry (a 2^j + u, a' 2^j + v) = H_m[a][a'] (-1)^popcount(u & v)
+  OuterTable t;
+  t.m = static_cast<int>(mm);
+  t.words = (t.m + 31) / 32;
+  t.h.assign(static_cast<size_t>(t.m) * t.m, 0);
+  const int B = 1 << j;
+  for (int r = 0; r < t.m; ++r)
+    for (int c = 0; c < t.m; ++c) {
+      const int syl = (__builtin_popcount(static_cast<unsigned>((r % B) & (c % B))) & 1) ? -1 : 1;
+      t.h[static_cast<size_t>(r) * t.m + c] = static_cast<int8_t>(base[static_cast<size_t>(r / B) * m + c / B] * syl);
+    }
+  t.mask.assign(static_cast<size_t>(t.m) * t.words, 0u);
+  t.mask_t.assign(static_cast<size_t>(t.m) * t.words, 0u);
+  for (int r = 0; r < t.m; ++r)
+    for (int c = 0; c < t.m; ++c)
+      if (t.h[static_cast<size_t>(r) * t.m + c] < 0) {
+        t.mask[static_cast<size_t>(r) * t.words + c / 32] |= 1u << (c % 32);
+        t.mask_t[static_cast<size_t>(c) * t.words + r / 32] |= 1u << (r % 32);
+      }
+  return &cache.emplace(std::make_pair(m, j), std::move(t)).first->second;
+}
+
 }  // namespace signrot

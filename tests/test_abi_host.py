@@ -235,6 +235,8 @@ def test_rotate_kernel_choice():
             assert name == "rq_mfma28_w7"
         elif n in (4096, 8192, 16384):
             assert name == "rq_mfma32_w8"
+        elif n in (2048, 32768):  # Sylvester read as 16 x 128 and 128 x 256
+            assert name == "rq_outer_mfma", (n, name)
         else:
             assert name == "rq_generic", (n, name)
     assert R.kernel_name(6) is None
@@ -279,7 +281,9 @@ def _expected_kernel(n):
     """The dispatch rule restated: the 2^k and 28 * 2^k MFMA kernels for their
     widths; the outer-order kernel for other Paley orders with 32 <= 2^k <= 256
     whose (K chunks, column tiles) is in its table and whose work-group fits 16
-    waves with a staging unit per thread; the generic kernel otherwise."""
+    waves with a staging unit per thread, or for a width that reaches such a
+    shape when Sylvester bits join the outer factor (2^k > 256, or a
+    Sylvester width without its own kernel); the generic kernel otherwise."""
     m, k = O.factor(n)
     if n in (4096, 8192, 16384):
         return "rq_mfma32_w8"
@@ -287,12 +291,23 @@ def _expected_kernel(n):
         return "rq_mfma28_w7"
     if n == 28672:
         return "rq_mfma56_w14"
-    if m > 1 and m != 28 and 5 <= k <= 8:
-        kc, ntl = (m + 31) // 32, 1 << (k - 4)
+    def outer_ok(mm, kk):
+        if mm <= 1 or mm == 28 or mm % 4 or mm > 512 or not 5 <= kk <= 8:
+            return False
+        kc, ntl = (mm + 31) // 32, 1 << (kk - 4)
         mtw = OUTER_TABLE.get((kc, ntl))
-        if mtw:
-            waves = -(-(-(-m // 16)) // mtw)
-            if waves <= 16 and m * ntl <= 64 * waves * ((ntl * mtw + 3) // 4):
+        if not mtw:
+            return False
+        waves = -(-(-(-mm // 16)) // mtw)
+        return waves <= 16 and mm * ntl <= 64 * waves * ((ntl * mtw + 3) // 4)
+
+    if outer_ok(m, k):
+        return "rq_outer_mfma"
+    # the same H read with `fold` Sylvester bits moved into the outer factor
+    if m == 1 or (m != 28 and k > 8):
+        for kk in (7, 8, 5, 6):
+            fold = k - kk
+            if fold >= (2 if m == 1 else 1) and outer_ok(m << fold, kk):
                 return "rq_outer_mfma"
     return "rq_generic"
 

@@ -5,7 +5,8 @@ m - 1 = 11, 19, 43, 107, 139, 343, ...; Paley II for m / 2 - 1 = 5, 9, 13,
 kernel's table run it (every instantiated shape appears below); the others
 run the generic kernel.  The oracle builds H_m by its own finite-field
 arithmetic (numpy), the library by its own (C++).  The last test takes one
-width for each remaining shape of the MFMA kernel's table.
+width for each remaining shape of the MFMA kernel's table, and the widths
+that reach it with Sylvester bits moved into the outer factor.
 
 Tolerances are the ones in parity.py (rotated values within 1e-5 of the
 token's max |y|, scale and zero-point within 1e-6, codes bit-exact except at
@@ -31,6 +32,11 @@ pytestmark = pytest.mark.gpu
 # MLP widths of common models (11008, 13824, 18944) plus two-factor widths
 WIDTHS = [12, 20, 24, 40, 72, 344, 1000, 2560, 4864, 5120, 5632, 8960, 11008, 13824, 17408, 18944, 24576, 27648]
 CHEAP = [n for n in WIDTHS if n <= 8960]
+# widths read with Sylvester bits moved into the outer factor (2^k > 256, or
+# a Sylvester width without its own kernel): n -> (outer order, 2^k) the
+# MFMA kernel sees
+FOLDED = {128: (4, 32), 256: (8, 32), 512: (4, 128), 1024: (8, 128), 2048: (16, 128), 6144: (48, 128),
+          10240: (80, 128), 12288: (96, 128), 20480: (160, 128), 24576: (96, 256), 32768: (128, 256)}
 # the kernel each width runs: (K chunks, column tiles) of the MFMA kernel's table
 OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5120: (1, 16), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
               13824: (4, 8), 17408: (3, 16), 18944: (5, 8), 27648: (4, 16)}
@@ -59,6 +65,8 @@ def test_widths_use_the_intended_outer_orders_and_kernels():
         assert m not in (1, 28) and R.outer_order(n) == m, n
         if n in OUTER_MFMA:
             assert OUTER_MFMA[n] == ((m + 31) // 32, (1 << k) // 16), n
+            assert R.kernel_name(n) == "rq_outer_mfma", n
+        elif n in FOLDED:
             assert R.kernel_name(n) == "rq_outer_mfma", n
         else:
             assert R.kernel_name(n) == "rq_generic", n
@@ -214,14 +222,14 @@ MORE_SHAPES = {(1, 2): 384, (1, 4): 768, (1, 16): 3072, (2, 2): 1152, (2, 4): 23
                (7, 2): 6272, (7, 4): 12544, (8, 2): 7296, (8, 4): 14592, (9, 2): 8832, (10, 2): 9600, (12, 2): 11648}
 
 
-@pytest.mark.parametrize("n", sorted(MORE_SHAPES.values()))
+@pytest.mark.parametrize("n", sorted(MORE_SHAPES.values()) + sorted(FOLDED))
 def test_every_mfma_shape_matches_oracle(n):
     """For each remaining shape: the calibrated sign vector and a random one
     through the d-vector entry point against the oracle, the outlier form
     bit-equal to the vector form, and the integer zero-point form against the
     oracle."""
     m, k = O.factor(n)
-    assert MORE_SHAPES[((m + 31) // 32, (1 << k) // 16)] == n
+    assert n in FOLDED or MORE_SHAPES[((m + 31) // 32, (1 << k) // 16)] == n
     assert R.kernel_name(n) == "rq_outer_mfma"
     t = 19
     bits = W.random_rows(t, n, seed=n + 7, scale=0.8)
