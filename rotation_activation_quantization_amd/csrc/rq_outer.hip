@@ -18,7 +18,8 @@ int outer_mtw(int kc, int ntl) {
 }  // namespace
 
 bool rq_outer_supports(int m, int k) {
-  if (m <= 1 || m == 28 || m % 4 != 0 || m > kMaxOuter || k < 5 || k > 8) return false;
+  // (m = 28 with 2^k = 128 .. 512 never gets here: the fast kernels take it)
+  if (m <= 1 || m % 4 != 0 || m > kMaxOuter || k < 5 || k > 8) return false;
   const int kc = (m + 31) / 32;
   const int ntl = 1 << (k - 4);
   const int mtw = outer_mtw(kc, ntl);

@@ -235,7 +235,7 @@ def test_rotate_kernel_choice():
             assert name == "rq_mfma28_w7"
         elif n in (4096, 8192, 16384):
             assert name == "rq_mfma32_w8"
-        elif n in (2048, 32768):  # Sylvester read as 16 x 128 and 128 x 256
+        elif n in (2048, 32768, 1792):  # Sylvester read as 16 x 128 and 128 x 256; 28 x 64
             assert name == "rq_outer_mfma", (n, name)
         else:
             assert name == "rq_generic", (n, name)
@@ -292,7 +292,7 @@ def _expected_kernel(n):
     if n == 28672:
         return "rq_mfma56_w14"
     def outer_ok(mm, kk):
-        if mm <= 1 or mm == 28 or mm % 4 or mm > 512 or not 5 <= kk <= 8:
+        if mm <= 1 or mm % 4 or mm > 512 or not 5 <= kk <= 8:
             return False
         kc, ntl = (mm + 31) // 32, 1 << (kk - 4)
         mtw = OUTER_TABLE.get((kc, ntl))
