@@ -142,7 +142,7 @@ def test_zint_matches_oracle(n):
     compare_zint(y, codes, scale, zero, f"paley zint n={n}")
 
 
-@pytest.mark.parametrize("n", [40, 1000, 5120, 11008, 13824])
+@pytest.mark.parametrize("n", [40, 1000, 2048, 5120, 11008, 13824, 24576])
 def test_fold_weights_matches_oracle(n):
     g = np.random.default_rng([42, n])
     rows = 33
