@@ -269,6 +269,20 @@ int signrot_debug_h28(int8_t* out);
  */
 int signrot_debug_outer(int m, int8_t* out);
 
+/*
+ * The outer factor the rotate kernel uses when it reads n = m * 2^k as
+ * (m 2^fold) * 2^(k - fold): H_m (x) Syl_{2^fold}, entry
+ * (a 2^fold + u, a' 2^fold + v) = H_m[a][a'] (-1)^popcount(u & v), with
+ * m = 1 (the Sylvester matrix alone), 28, or a Paley order.  Written
+ * row-major to host memory out[(m 2^fold)^2].  Host-only.  SIGNROT_EINVAL
+ * when m 2^fold > 512 or m has no construction.
+ */
+int signrot_debug_outer_folded(int m, int fold, int8_t* out);
+
+/* How many Sylvester index bits the rotate kernel for n moves into its outer
+ * factor (0: none), or -1 when n is unsupported.  Host-only. */
+int signrot_outer_fold(int64_t n);
+
 /* Which kernel variant signrot_rotate_quant_int4 would launch for n (a
  * static string naming it), or NULL when n is unsupported:
  *   "rq_mfma32_w8"   n = 4096, 8192, 16384 (Sylvester);

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
     L.signrot_debug_outer.restype = ctypes.c_int
     L.signrot_outer_order.argtypes = [i64]
     L.signrot_outer_order.restype = ctypes.c_int
+    L.signrot_debug_outer_folded.argtypes = [ctypes.c_int, ctypes.c_int, vp]
+    L.signrot_debug_outer_folded.restype = ctypes.c_int
+    L.signrot_outer_fold.argtypes = [i64]
+    L.signrot_outer_fold.restype = ctypes.c_int
     L.signrot_kernel_name.argtypes = [i64]
     L.signrot_kernel_name.restype = ctypes.c_char_p
     _lib = L
@@ -92,7 +96,9 @@ EXPORTED = (
     "signrot_last_error",
     "signrot_debug_h28",
     "signrot_debug_outer",
+    "signrot_debug_outer_folded",
     "signrot_outer_order",
+    "signrot_outer_fold",
     "signrot_kernel_name",
 )
 
@@ -123,6 +129,21 @@ def debug_outer(m: int):
     buf = (ctypes.c_int8 * (m * m))()
     check(lib().signrot_debug_outer(int(m), ctypes.addressof(buf)), "signrot_debug_outer")
     return [list(buf[r * m:(r + 1) * m]) for r in range(m)]
+
+
+def debug_outer_folded(m: int, fold: int):
+    """The library's folded outer factor H_m (x) Syl_{2^fold} (host only)."""
+    import numpy as np
+
+    mm = int(m) << int(fold)
+    buf = (ctypes.c_int8 * (mm * mm))()
+    check(lib().signrot_debug_outer_folded(int(m), int(fold), ctypes.addressof(buf)), "signrot_debug_outer_folded")
+    return np.frombuffer(buf, dtype=np.int8).reshape(mm, mm).copy()
+
+
+def outer_fold(n: int) -> int:
+    """Sylvester bits the rotate kernel for n folds into its outer factor."""
+    return int(lib().signrot_outer_fold(int(n)))
 
 
 def debug_h28():

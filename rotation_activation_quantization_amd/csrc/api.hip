@@ -226,6 +226,22 @@ int signrot_debug_outer(int m, int8_t* out) {
   return SIGNROT_OK;
 }
 
+int signrot_debug_outer_folded(int m, int fold, int8_t* out) {
+  g_last_error[0] = '\0';
+  if (!out) return fail_einval("out is NULL");
+  if (m < 1 || fold < 0 || fold > 9 || (static_cast<int64_t>(m) << fold) > kMaxOuter)
+    return fail_einval("m * 2^fold out of range");
+  const OuterTable* t = outer_table_folded(m, fold);
+  if (!t) return fail_einval("no construction of H_m (x) Syl_{2^fold}");
+  memcpy(out, t->h.data(), static_cast<size_t>(t->m) * t->m);
+  return SIGNROT_OK;
+}
+
+int signrot_outer_fold(int64_t n) {
+  const Shape sh = factor_n(n);
+  return sh.ok ? rq_plan_for(sh).fold : -1;
+}
+
 const char* signrot_kernel_name(int64_t n) {
   const Shape sh = factor_n(n);
   if (!sh.ok) return nullptr;

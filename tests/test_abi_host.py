@@ -324,3 +324,26 @@ def test_kernel_dispatch_rule():
         seen.add(want)
     assert seen == {"rq_mfma32_w8", "rq_mfma28_w7", "rq_mfma56_w14", "rq_outer_mfma", "rq_generic"}
 
+
+@pytest.mark.parametrize("m,fold", [(1, 2), (1, 4), (1, 7), (12, 3), (20, 3), (12, 5), (28, 1), (28, 4), (108, 2),
+                                    (44, 3), (344, 0)])
+def test_folded_outer_factor_equals_kronecker_of_oracle_factors(m, fold):
+    """The library's folded table (its own C++ H_m and Sylvester) against the
+    Kronecker product of the oracle's H_m and Sylvester matrices."""
+    base = np.ones((1, 1), np.int64) if m == 1 else (O.paley28() if m == 28 else O.outer_matrix(m)).astype(np.int64)
+    want = np.kron(base, O.sylvester(fold).astype(np.int64)).astype(np.int8)
+    assert np.array_equal(R.debug_outer_folded(m, fold), want)
+
+
+def test_fold_choice_for_wide_widths(L):
+    """The fold the rotate kernel takes: 2^(k - fold) = 128 first, then 256."""
+    want = {24576: 4, 20480: 3, 12288: 3, 10240: 2, 6144: 2, 32768: 7, 2048: 4, 1024: 3, 512: 2, 256: 3, 128: 2,
+            11008: 0, 14336: 0, 4096: 0, 22016: 0}
+    for n, f in want.items():
+        assert R.outer_fold(n) == f, n
+    assert R.outer_fold(6) == -1
+    buf = (ctypes.c_int8 * 16)()
+    assert L.signrot_debug_outer_folded(3, 0, buf) == R.SIGNROT_EINVAL
+    assert L.signrot_debug_outer_folded(344, 1, buf) == R.SIGNROT_EINVAL  # order 688 > 512
+    assert L.signrot_debug_outer_folded(12, 1, None) == R.SIGNROT_EINVAL
+
