@@ -36,7 +36,7 @@ CHEAP = [n for n in WIDTHS if n <= 8960]
 # a Sylvester width without its own kernel): n -> (outer order, 2^k) the
 # MFMA kernel sees
 FOLDED = {128: (4, 32), 256: (8, 32), 512: (4, 128), 1024: (8, 128), 2048: (16, 128), 6144: (48, 128),
-          10240: (80, 128), 12288: (96, 128), 20480: (160, 128), 24576: (96, 256), 32768: (128, 256)}
+          10240: (80, 128), 12288: (96, 128), 20480: (160, 128), 24576: (192, 128), 32768: (128, 256)}
 # the kernel each width runs: (K chunks, column tiles) of the MFMA kernel's table
 OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5120: (1, 16), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
               13824: (4, 8), 17408: (3, 16), 18944: (5, 8), 27648: (4, 16)}
@@ -68,6 +68,8 @@ def test_widths_use_the_intended_outer_orders_and_kernels():
             assert R.kernel_name(n) == "rq_outer_mfma", n
         elif n in FOLDED:
             assert R.kernel_name(n) == "rq_outer_mfma", n
+            f = R.outer_fold(n)
+            assert (m << f, 1 << (k - f)) == FOLDED[n], n
         else:
             assert R.kernel_name(n) == "rq_generic", n
 
