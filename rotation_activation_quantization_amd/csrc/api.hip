@@ -139,7 +139,10 @@ RqPlan rq_plan_for(const Shape& sh) {
 RqKernel rq_kernel_for(const Shape& sh) { return rq_plan_for(sh).kind; }
 
 // Fills the outer-factor fields of a (the device sign tables it needs); with
-// a fold, also the outer order and Sylvester exponent the kernel sees.
+// a fold, also the outer order and Sylvester exponent the kernel sees.  The
+// fast kernels take H28 by value (h28mask) and read no table, so their calls
+// never allocate one: after the first call on a device, a captured call makes
+// no runtime allocation.
 hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
   hipError_t he = hipSuccess;
   const RqPlan p = rq_plan_for(sh);
@@ -148,7 +151,7 @@ hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
   a.hw = (a.m + 31) / 32;
   a.hm = nullptr;
   a.hmt = nullptr;
-  if (a.m > 1) {
+  if (a.m > 1 && p.kind != RqKernel::kFast) {
     if (!(a.hm = outer_mask_device(sh.m, &he, false, p.fold))) return he;
     if (p.kind == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, true, p.fold))) return he;
   }
