@@ -47,7 +47,8 @@ KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_c
                   "rotation_activation_quantization_amd/build.py")
 GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h",
                    "rotation_activation_quantization_amd/build.py")
-OUTER_SOURCES = (_CSRC + "rq_outer_impl.h", _CSRC + "rq_outer.hip", _CSRC + "rq_outer_t2.hip", _CSRC + "rq_outer_t4.hip",
+OUTER_SOURCES = (_CSRC + "rq_outer_impl.h", _CSRC + "rq_outer.hip", _CSRC + "rq_outer_t1.hip", _CSRC + "rq_outer_t2.hip",
+                 _CSRC + "rq_outer_t4.hip",
                  _CSRC + "rq_outer_t8.hip", _CSRC + "rq_outer_t16.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h",
                  _CSRC + "internal.h", "rotation_activation_quantization_amd/build.py")
 TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"

@@ -20,6 +20,7 @@ SOURCES = [
     "rq_generic.hip",
     "rq_fast.hip",
     "rq_outer.hip",
+    "rq_outer_t1.hip",
     "rq_outer_t2.hip",
     "rq_outer_t4.hip",
     "rq_outer_t8.hip",

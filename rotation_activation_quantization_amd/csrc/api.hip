@@ -125,8 +125,8 @@ RqPlan rq_plan_for(const Shape& sh) {
   if (rq_fast_supports(sh.n, sh.k, sh.m28)) return {RqKernel::kFast, 0};
   if (rq_outer_supports(sh.m, sh.k)) return {RqKernel::kOuter, 0};
   if (sh.m == 1 || (sh.m != 28 && sh.k > 8)) {
-    // 2^(k - fold) = 128 first (the kernel's best column-tile count), then 256, 32, 64
-    for (const int kk : {7, 8, 5, 6}) {
+    // 2^(k - fold) = 128 first (the kernel's best column-tile count), then 256, 32, 64, 16
+    for (const int kk : {7, 8, 5, 6, 4}) {
       const int fold = sh.k - kk;
       const int64_t mm = static_cast<int64_t>(sh.m) << (fold > 0 ? fold : 0);
       if (fold >= (sh.m == 1 ? 2 : 1) && mm <= kMaxOuter && rq_outer_supports(static_cast<int>(mm), kk))

@@ -1,5 +1,5 @@
 // Outer-order MFMA kernel: which shapes are built, and the launch dispatch.
-// The kernel itself is rq_outer_impl.h; rq_outer_t{2,4,8,16}.hip
+// The kernel itself is rq_outer_impl.h; rq_outer_t{1,2,4,8,16}.hip
 // instantiate it per column-tile count.
 #include "rq_outer_impl.h"
 
@@ -8,6 +8,7 @@ namespace signrot {
 namespace {
 int outer_mtw(int kc, int ntl) {
   switch (ntl) {
+    case 1: return rq_outer_mtw_t1(kc);
     case 2: return rq_outer_mtw_t2(kc);
     case 4: return rq_outer_mtw_t4(kc);
     case 8: return rq_outer_mtw_t8(kc);
@@ -19,7 +20,7 @@ int outer_mtw(int kc, int ntl) {
 
 bool rq_outer_supports(int m, int k) {
   // (m = 28 with 2^k = 128 .. 512 never gets here: the fast kernels take it)
-  if (m <= 1 || m % 4 != 0 || m > kMaxOuter || k < 5 || k > 8) return false;
+  if (m <= 1 || m % 4 != 0 || m > kMaxOuter || k < 4 || k > 8) return false;
   const int kc = (m + 31) / 32;
   const int ntl = 1 << (k - 4);
   const int mtw = outer_mtw(kc, ntl);
@@ -32,6 +33,7 @@ bool rq_outer_supports(int m, int k) {
 
 hipError_t launch_rq_outer(const RqArgs& a, hipStream_t s) {
   switch (1 << (a.k - 4)) {
+    case 1: return rq_outer_launch_t1(a, s);
     case 2: return rq_outer_launch_t2(a, s);
     case 4: return rq_outer_launch_t4(a, s);
     case 8: return rq_outer_launch_t8(a, s);

@@ -55,8 +55,9 @@ using namespace wave;
 
 template <int KC, int NTL, int MTW>
 struct OuterShape {
-  static constexpr int LGN = NTL == 2 ? 1 : NTL == 4 ? 2 : NTL == 8 ? 3 : 4;
-  static_assert(NTL == (1 << LGN) && NTL >= 2 && NTL <= 16, "2 to 16 column tiles");
+  static constexpr int LGN = NTL == 1 ? 0 : NTL == 2 ? 1 : NTL == 4 ? 2 : NTL == 8 ? 3 : 4;
+  static_assert(NTL == (1 << LGN) && NTL >= 1 && NTL <= 16, "1 to 16 column tiles");
+  static_assert(NTL > 1 || MTW % 2 == 0, "one column tile: an even number of M-tiles per wave");
   static_assert(KC >= 1 && KC <= 16, "outer order up to 512");
   static constexpr int KB = 4 + LGN;          // log2 B
   static constexpr int B = 16 * NTL;
@@ -76,6 +77,19 @@ struct OuterShape {
 template <int LGN>
 __device__ __forceinline__ uint32_t lds_row(uint32_t b) {
   return (b >> LGN) | ((b & ((1u << LGN) - 1u)) << 4);
+}
+
+// One column tile (2^k = 16): lane nl reads input index one_tile_in(nl);
+// after the four DPP stages it holds output one_tile_out(nl), and lanes nl
+// and nl ^ 1 hold adjacent outputs (one_tile_out(nl ^ 1) = one_tile_out(nl) ^ 1),
+// so a code byte pairs the two lanes of a quad half.  (With the usual input
+// nl ^ kXLane the pairs would sit six lanes apart.)
+__device__ __forceinline__ int one_tile_in(int nl) {
+  const int v = nl ^ kXLane;
+  return v ^ ((v >> 2) & 1);
+}
+__device__ __forceinline__ int one_tile_out(int nl) {
+  return (nl & 9) ^ ((nl & 2) ? 6 : 0) ^ ((nl & 4) ? 3 : 0);
 }
 
 template <int KC, int NTL, int MTW, bool GENERAL, bool YOUT, bool ZINT = false>
@@ -185,12 +199,13 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
   };
 
   // operand read offset of this lane inside a buffer (N-tile part added per nt)
-  const uint32_t lane_off = static_cast<uint32_t>((nl ^ kXLane) ^ cbh) * RS + 16u * g4;
+  const int lane_in = NTL == 1 ? one_tile_in(nl) : (nl ^ kXLane);
+  const uint32_t lane_off = static_cast<uint32_t>(lane_in ^ cbh) * RS + 16u * g4;
   const float gdpp0 = (((nl >> 0) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
   const float gdpp1 = (((nl >> 1) ^ (nl >> 2)) & 1) ? -1.0f : 1.0f;
   const float gdpp2 = ((nl >> 2) & 1) ? -1.0f : 1.0f;
   const float gdpp3 = ((nl >> 3) & 1) ? -1.0f : 1.0f;
-  const int outm = lane_perm(nl);
+  const int outm = NTL == 1 ? one_tile_out(nl) : lane_perm(nl);
 
   // rows a' of this lane: 16 (w MTW + i) + 4 g4 + r
   bool rv[MTW][4];
@@ -262,7 +277,7 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
 #pragma unroll
     for (int i = 0; i < MTW; ++i) {
       float(&vi)[NTL * 4] = *reinterpret_cast<float(*)[NTL * 4]>(v + i * NTL * 4);
-      reg_stage<NTL, 0>(vi);
+      if constexpr (NTL >= 2) reg_stage<NTL, 0>(vi);
       if constexpr (NTL >= 4) reg_stage<NTL, 1>(vi);
       if constexpr (NTL >= 8) reg_stage<NTL, 2>(vi);
       if constexpr (NTL >= 16) reg_stage<NTL, 3>(vi);
@@ -294,10 +309,15 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (!rv[i][r]) continue;
+        if constexpr (NTL == 1) {
+          mn = fmin_raw(mn, v[i * 4 + r]);
+          mx = fmax_raw(mx, v[i * 4 + r]);
+        } else {
 #pragma unroll
-        for (int t = 0; t < NTL; t += 2) {
-          min3_acc(mn, v[(i * NTL + t) * 4 + r], v[(i * NTL + t + 1) * 4 + r]);
-          max3_acc(mx, v[(i * NTL + t) * 4 + r], v[(i * NTL + t + 1) * 4 + r]);
+          for (int t = 0; t < NTL; t += 2) {
+            min3_acc(mn, v[(i * NTL + t) * 4 + r], v[(i * NTL + t + 1) * 4 + r]);
+            max3_acc(mx, v[(i * NTL + t) * 4 + r], v[(i * NTL + t + 1) * 4 + r]);
+          }
         }
       }
     wave_minmax(mn, mx);
@@ -334,13 +354,31 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
       a.zero[row] = ZINT ? zq : (qp.degenerate ? -((mn + shift) * a.inv_sqrt_n) : -(mn + shift) * qp.inv);
     }
     uint8_t* crow = a.codes + row * static_cast<int64_t>(n / 2);
+    if constexpr (NTL == 1) {
+      // one code per lane and row: every lane rounds its value and takes its
+      // partner's code from lane nl ^ 1; the lane holding the even channel
+      // stores the byte
+#pragma unroll
+      for (int i = 0; i < MTW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float f = fmaf(v[i * 4 + r], qp.inv, cq);
+          if constexpr (ZINT) f = fminf(f, 15.0f);
+          const int q = static_cast<int>(__builtin_amdgcn_cvt_pk_u8_f32(f, 0, 0u));
+          const int qp1 = __builtin_amdgcn_mov_dpp(q, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+          if (!rv[i][r]) continue;
+          const int j0 = (16 * (w * MTW + i) + 4 * g4 + r) * B + outm;
+          if ((outm & 1) == 0) crow[j0 / 2] = static_cast<uint8_t>(q | (qp1 << 4));
+          if (YOUT) a.yout[row * static_cast<int64_t>(n) + j0] = (v[i * 4 + r] + shift) * a.inv_sqrt_n;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < MTW; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (!rv[i][r]) continue;
+        if (NTL == 1 || !rv[i][r]) continue;
         const int j0 = (16 * (w * MTW + i) + 4 * g4 + r) * B + NTL * outm;
-        uint32_t q[(NTL + 7) / 8];
+        uint32_t q[(NTL + 7) / 8] = {};
 #pragma unroll
         for (int u = 0; u < (NTL + 7) / 8; ++u) {
           uint32_t ev = 0u, od = 0u;
@@ -359,14 +397,14 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
           q[u] = ev | (od << 4);
         }
         uint8_t* cp = crow + j0 / 2;
-        if constexpr (NTL == 2) *cp = static_cast<uint8_t>(q[0]);
+        if constexpr (NTL <= 2) *cp = static_cast<uint8_t>(q[0]);
         else if constexpr (NTL == 4) *reinterpret_cast<uint16_t*>(cp) = static_cast<uint16_t>(q[0]);
         else if constexpr (NTL == 8) *reinterpret_cast<uint32_t*>(cp) = q[0];
         else *reinterpret_cast<uint2*>(cp) = make_uint2(q[0], q[1]);
         if (YOUT) {
           float* yp = a.yout + row * static_cast<int64_t>(n) + j0;
 #pragma unroll
-          for (int t = 0; t < NTL; t += 2) {
+          for (int t = 0; t + 1 < NTL; t += 2) {
             const float y0 = (v[(i * NTL + t) * 4 + r] + shift) * a.inv_sqrt_n;
             const float y1 = (v[(i * NTL + t + 1) * 4 + r] + shift) * a.inv_sqrt_n;
             *reinterpret_cast<float2*>(yp + t) = make_float2(y0, y1);
@@ -446,6 +484,9 @@ hipError_t launch_outer_shape(const RqArgs& a, hipStream_t stream) {
 // launch bound (ceil(2 KC / MTW) waves per work-group) leaves, without
 // spills, and the work-group within 16 waves.  One translation unit per
 // column-tile count instantiates them.
+#define SR_OUTER_SHAPES_T1(X)                                                                                   \
+  X(1, 1, 2) X(2, 1, 2) X(3, 1, 2) X(4, 1, 2) X(5, 1, 2) X(6, 1, 2) X(7, 1, 2) X(8, 1, 2) X(9, 1, 2) X(10, 1, 2) \
+  X(11, 1, 2) X(12, 1, 2)
 #define SR_OUTER_SHAPES_T2(X) \
   X(1, 2, 1) X(2, 2, 1) X(3, 2, 1) X(4, 2, 1) X(5, 2, 1) X(6, 2, 1) X(7, 2, 1) X(8, 2, 1) X(9, 2, 2) X(10, 2, 2) \
   X(11, 2, 2) X(12, 2, 2)
@@ -457,6 +498,7 @@ hipError_t launch_outer_shape(const RqArgs& a, hipStream_t stream) {
 #define SR_OUTER_DECLARE(NTL)                                \
   int rq_outer_mtw_t##NTL(int kc);                           \
   hipError_t rq_outer_launch_t##NTL(const RqArgs& a, hipStream_t s);
+SR_OUTER_DECLARE(1)
 SR_OUTER_DECLARE(2)
 SR_OUTER_DECLARE(4)
 SR_OUTER_DECLARE(8)

@@ -272,7 +272,8 @@ def test_header_is_plain_c(tmp_path):
 
 
 # (K chunks, column tiles) -> M-tiles per wave of the outer-order MFMA kernel
-OUTER_TABLE = {**{(kc, 2): 1 for kc in range(1, 9)}, **{(kc, 2): 2 for kc in range(9, 13)},
+OUTER_TABLE = {**{(kc, 1): 2 for kc in range(1, 13)},
+               **{(kc, 2): 1 for kc in range(1, 9)}, **{(kc, 2): 2 for kc in range(9, 13)},
                **{(kc, 4): 1 for kc in range(1, 9)}, **{(kc, 8): 1 for kc in range(1, 7)},
                **{(kc, 16): 1 for kc in range(1, 5)}}
 
@@ -280,7 +281,7 @@ OUTER_TABLE = {**{(kc, 2): 1 for kc in range(1, 9)}, **{(kc, 2): 2 for kc in ran
 def _expected_kernel(n):
     """The dispatch rule restated: the 2^k and 28 * 2^k MFMA kernels for their
     widths; the outer-order kernel for other Paley orders with 32 <= 2^k <= 256
-    whose (K chunks, column tiles) is in its table and whose work-group fits 16
+    (16 <= 2^k <= 256) whose (K chunks, column tiles) is in its table and whose work-group fits 16
     waves with a staging unit per thread, or for a width that reaches such a
     shape when Sylvester bits join the outer factor (2^k > 256, or a
     Sylvester width without its own kernel); the generic kernel otherwise."""
@@ -292,7 +293,7 @@ def _expected_kernel(n):
     if n == 28672:
         return "rq_mfma56_w14"
     def outer_ok(mm, kk):
-        if mm <= 1 or mm % 4 or mm > 512 or not 5 <= kk <= 8:
+        if mm <= 1 or mm % 4 or mm > 512 or not 4 <= kk <= 8:
             return False
         kc, ntl = (mm + 31) // 32, 1 << (kk - 4)
         mtw = OUTER_TABLE.get((kc, ntl))
@@ -305,7 +306,7 @@ def _expected_kernel(n):
         return "rq_outer_mfma"
     # the same H read with `fold` Sylvester bits moved into the outer factor
     if m == 1 or (m != 28 and k > 8):
-        for kk in (7, 8, 5, 6):
+        for kk in (7, 8, 5, 6, 4):
             fold = k - kk
             if fold >= (2 if m == 1 else 1) and outer_ok(m << fold, kk):
                 return "rq_outer_mfma"

@@ -2,8 +2,8 @@
 factor H_m is a Paley matrix of an order other than 28 (Paley I for
 m - 1 = 11, 19, 43, 107, 139, 343, ...; Paley II for m / 2 - 1 = 5, 9, 13,
 49, 73, ...).  Widths with 32 <= n / m <= 256 in the outer-order MFMA
-kernel's table run it (every instantiated shape appears below); the others
-run the generic kernel.  The oracle builds H_m by its own finite-field
+kernel's table (16 <= n / m <= 256) run it; the others run the generic
+kernel.  The oracle builds H_m by its own finite-field
 arithmetic (numpy), the library by its own (C++).  The last test takes one
 width for each remaining shape of the MFMA kernel's table, and the widths
 that reach it with Sylvester bits moved into the outer factor.
@@ -35,7 +35,7 @@ CHEAP = [n for n in WIDTHS if n <= 8960]
 # widths read with Sylvester bits moved into the outer factor (2^k > 256, or
 # a Sylvester width without its own kernel): n -> (outer order, 2^k) the
 # MFMA kernel sees
-FOLDED = {128: (4, 32), 256: (8, 32), 512: (4, 128), 1024: (8, 128), 2048: (16, 128), 6144: (48, 128),
+FOLDED = {64: (4, 16), 128: (4, 32), 256: (8, 32), 512: (4, 128), 1024: (8, 128), 2048: (16, 128), 6144: (48, 128),
           10240: (80, 128), 12288: (96, 128), 20480: (160, 128), 24576: (192, 128), 32768: (128, 256)}
 # the kernel each width runs: (K chunks, column tiles) of the MFMA kernel's table
 OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5120: (1, 16), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
@@ -221,7 +221,9 @@ def test_full_size_workload_sampled():
 # (K chunks, column tiles) -> n
 MORE_SHAPES = {(1, 2): 384, (1, 4): 768, (1, 16): 3072, (2, 2): 1152, (2, 4): 2304, (2, 16): 9216, (3, 2): 2176,
                (3, 8): 8704, (4, 2): 3200, (4, 4): 6400, (5, 2): 4224, (6, 2): 5248, (6, 4): 10496, (6, 8): 20992,
-               (7, 2): 6272, (7, 4): 12544, (8, 2): 7296, (8, 4): 14592, (9, 2): 8832, (10, 2): 9600, (12, 2): 11648}
+               (7, 2): 6272, (7, 4): 12544, (8, 2): 7296, (8, 4): 14592, (9, 2): 8832, (10, 2): 9600, (12, 2): 11648,
+               # one column tile (2^k = 16): 5504 = 344 * 16 is half of 11008
+               (1, 1): 192, (2, 1): 704, (4, 1): 1728, (5, 1): 2368, (11, 1): 5504, (12, 1): 5824}
 
 
 @pytest.mark.parametrize("n", sorted(MORE_SHAPES.values()) + sorted(FOLDED))
