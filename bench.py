@@ -42,15 +42,13 @@ WORKLOAD = "n14336_t8192"
 BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # Sources that define the timed kernel; the HBM traffic measured with
 # rocprofv3 counters is reported only while they are unchanged.
+# (plus the compile flags, build.COMMON)
 _CSRC = "rotation_activation_quantization_amd/csrc/"
-KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h", _CSRC + "internal.h",
-                  "rotation_activation_quantization_amd/build.py")
-GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h",
-                   "rotation_activation_quantization_amd/build.py")
+KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h", _CSRC + "internal.h")
+GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h")
 OUTER_SOURCES = (_CSRC + "rq_outer_impl.h", _CSRC + "rq_outer.hip", _CSRC + "rq_outer_t1.hip", _CSRC + "rq_outer_t2.hip",
-                 _CSRC + "rq_outer_t4.hip",
-                 _CSRC + "rq_outer_t8.hip", _CSRC + "rq_outer_t16.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h",
-                 _CSRC + "internal.h", "rotation_activation_quantization_amd/build.py")
+                 _CSRC + "rq_outer_t4.hip", _CSRC + "rq_outer_t8.hip", _CSRC + "rq_outer_t16.hip", _CSRC + "wave_ops.h",
+                 _CSRC + "device_common.h", _CSRC + "internal.h")
 TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"
 
 
@@ -59,12 +57,16 @@ def kernel_sources(kernel: str):
 
 
 def kernel_source_digest(kernel: str = "") -> str:
+    """sha256 over the kernel's sources and the compile flags."""
     import hashlib
+
+    from rotation_activation_quantization_amd import build as b
 
     h = hashlib.sha256()
     for p in kernel_sources(kernel):
         with open(os.path.join(HERE, p), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(b.COMMON).encode())
     return h.hexdigest()
 
 
