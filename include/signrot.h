@@ -288,12 +288,12 @@ int signrot_outer_fold(int64_t n);
  *   "rq_mfma32_w8"   n = 4096, 8192, 16384 (Sylvester);
  *   "rq_mfma28_w7"   n = 28 * 2^k, k = 7, 8, 9;
  *   "rq_mfma56_w14"  n = 28672;
- *   "rq_outer_mfma"  n = m * 2^k with 32 <= 2^k <= 256 and ceil(m / 32)
- *                    at most 12, 8, 6, 4 for 2^k = 32, 64, 128, 256 (11008,
- *                    13824, 18944, 8960, 27648, 5120, 896, 1792 among them),
- *                    and widths that reach such a shape with Sylvester bits
- *                    moved into the outer factor (24576, 20480, 12288, 10240,
- *                    6144, 128 .. 2048, 32768);
+ *   "rq_outer_mfma"  n = m * 2^k with 16 <= 2^k <= 256 and ceil(m / 32)
+ *                    at most 12, 12, 8, 6, 4 for 2^k = 16, 32, 64, 128, 256
+ *                    (11008, 13824, 18944, 8960, 27648, 5120, 5504, 896,
+ *                    1792 among them), and widths that reach such a shape
+ *                    with Sylvester bits moved into the outer factor (24576,
+ *                    20480, 12288, 10240, 6144, 64 .. 2048, 32768);
  *   "rq_generic"     every other supported n.
  * Host-only (no GPU needed). */
 const char* signrot_kernel_name(int64_t n);
