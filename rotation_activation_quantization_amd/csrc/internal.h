@@ -91,8 +91,8 @@ const char* rq_generic_name();
 bool rq_fast_supports(int n, int k, bool m28);
 hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s);
 const char* rq_fast_name(int n);
-// MFMA kernel for outer Paley orders m != 28 with 32 <= 2^k <= 256 (shapes in
-// its table); rq_outer_supports is host-only.
+// MFMA kernel for outer orders m (multiples of 4 up to 512) with
+// 16 <= 2^k <= 256 (shapes in its table); rq_outer_supports is host-only.
 bool rq_outer_supports(int m, int k);
 hipError_t launch_rq_outer(const RqArgs& a, hipStream_t s);
 const char* rq_outer_name();

@@ -1,9 +1,9 @@
 // Fused rotate + sign flip + per-token asymmetric INT4 for gfx950 when
 // n = m * 2^k with an outer factor H_m given by its sign tables (m a
 // multiple of 4 up to 512: a Paley matrix, possibly times a Sylvester factor)
-// and 32 <= 2^k <= 256: 11008 = 344 * 2^5, 13824 = 108 * 2^7,
-// 18944 = 148 * 2^7, 8960 = 140 * 2^6, 27648 = 108 * 2^8, 5120 = 20 * 2^8 and
-// the other shapes of the table at the end of this file.
+// and 16 <= 2^k <= 256: 11008 = 344 * 2^5, 13824 = 108 * 2^7,
+// 18944 = 148 * 2^7, 8960 = 140 * 2^6, 27648 = 108 * 2^8, 5120 = 20 * 2^8,
+// 5504 = 344 * 2^4 and the other shapes of the table at the end of this file.
 //
 // Method: explainer "SignRot for 4-bit LLM quantization -- Sign-adjusted
 // Hadamard rotation", paragraphs on rotation (every output a signed sum of all
