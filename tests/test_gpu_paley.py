@@ -255,3 +255,41 @@ def test_every_mfma_shape_matches_oracle(n):
     codes, scale, zero = to_np(R.rotate_quant_int4_zint(x, cal["c"], cal["sigma"]))
     compare_zint(O.rotate(O.bf16_bits_to_f64(bits), cal["d"]), codes, scale, zero, f"zint n={n}")
 
+
+
+@pytest.mark.parametrize("n", [11008, 24576])
+def test_graph_replays_match_eager_calls(n):
+    """The outer-order kernel captured in a HIP graph (after an eager call on
+    the device, which builds its sign tables): three replays, with other
+    eager work and synchronisations between them, each bit-equal to the
+    eager call on the same input."""
+    t = 8
+    bits = W.random_rows(t, n, seed=n + 11, scale=0.7, outlier=1300.0)
+    cal = O.calibrate(bits)
+    x = dev(bits)
+    ref = [v.clone() for v in R.rotate_quant_int4_outlier(x, cal["c"], cal["sigma"])]
+    codes = torch.empty_like(ref[0])
+    scale = torch.empty_like(ref[1])
+    zero = torch.empty_like(ref[2])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(3):
+                R.rotate_quant_int4_outlier(x, cal["c"], cal["sigma"], out=(codes, scale, zero))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        codes.zero_()
+        scale.zero_()
+        zero.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes, ref[0]) and torch.equal(scale, ref[1]) and torch.equal(zero, ref[2]), rep
+        other = R.rotate_quant_int4_outlier(x, cal["c"], cal["sigma"])  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other[0], ref[0])
+    del g
