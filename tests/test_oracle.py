@@ -48,6 +48,24 @@ def test_paley28_is_skew_hadamard():
     assert np.all(h[0] == 1)
 
 
+def test_paley28_fingerprints():
+    """The order-28 matrix the library and the oracle both build from Paley's
+    construction I over GF(27) = GF(3)[t]/(t^3 + 2t + 1): rows 1 and 2 as sign
+    strings, row 0 all +1, and the index-weighted sum of all entries.  A
+    relabelling of the field elements, another modulus or a transposed S would
+    keep H H^T = 28 I and H + H^T = 2 I but change these."""
+    h = O.paley28().astype(np.int64)
+
+    def signs(row):
+        return "".join("+" if v > 0 else "-" for v in row)
+
+    assert signs(h[0]) == "+" * 28
+    assert signs(h[1]) == "-+-++++----+---+--+++-+-++-+"
+    assert signs(h[2]) == "-++-+++-----++--+---++++-++-"
+    i, j = np.indices((28, 28))
+    assert int((h * (28 * i + j)).sum()) == 756
+
+
 def test_gf27_field_axioms():
     """The multiplication used for the quadratic character is a field: every
     nonzero element has an inverse and exactly 13 nonzero squares exist."""
@@ -391,6 +409,63 @@ def test_round_half_even_on_exact_ties():
     q, s, _ = O.quant_asym(y)
     assert s[0] == 1.0
     assert q[0].tolist() == [0, 0, 2, 2, 15]
+
+
+def test_code_position_hand_values():
+    """Quantizer paragraph: the position of a value among the 16 levels is
+    (y - mn) / s with s = (mx - mn) / 15.  Rows whose positions are exact
+    small numbers in either precision."""
+    y = np.array([[2.0, 4.0, 32.0, 17.0, 3.0], [-1.0, -1.0, -1.0, -1.0, -1.0]])
+    for prec in ("f64", "f32"):
+        p = O.code_position(y, prec)
+        assert p[0].tolist() == [0.0, 1.0, 15.0, 7.5, 0.5]
+        assert p[1].tolist() == [0.0] * 5  # mx == mn: s = 1, every value at level 0
+
+
+def test_code_position_against_exact_rationals():
+    """The float64 position is the exact rational (y - mn) / ((mx - mn) / 15)
+    to a few ulps; the binary32 one stays within binary32's error bound
+    2^-24 (4 r + 15), r = max|y| / s, and on the planted row it crosses the
+    half-integer that the exact position stays below, which is why the two
+    precisions pick different codes there."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(17)
+    rows = [rng.standard_normal(9) * rng.uniform(0.1, 10) + rng.uniform(-5, 5) for _ in range(40)]
+    planted = [-0.5411198139190674, 1.566705346107483, 2.2082173824310303]  # binary32 values
+    y = np.zeros((41, 9))
+    for i, r in enumerate(rows):
+        y[i] = r
+    y[40] = planted + [planted[0]] * 6
+    y32 = y.astype(np.float32).astype(np.float64)
+    p64 = O.code_position(y32, "f64")
+    p32 = O.code_position(y32, "f32")
+    for i in range(y32.shape[0]):
+        mn, mx = Fraction(y32[i].min()), Fraction(y32[i].max())
+        s = (mx - mn) / 15
+        r = float(max(abs(mn), abs(mx)) / s)
+        for j in range(y32.shape[1]):
+            exact = (Fraction(y32[i, j]) - mn) / s
+            assert abs(p64[i, j] - float(exact)) <= 4 * 2.0 ** -52 * max(1.0, float(exact))
+            assert abs(p32[i, j] - float(exact)) <= 2.0 ** -24 * (4 * r + 15)
+    exact = (Fraction(planted[1]) - Fraction(planted[0])) / ((Fraction(planted[2]) - Fraction(planted[0])) / 15)
+    assert exact < Fraction(23, 2) and p32[40, 1] > 11.5
+    q64, _, _ = O.quant_asym(y32[40:], "f64")
+    q32, _, _ = O.quant_asym(y32[40:], "f32")
+    assert (q64[0, 1], q32[0, 1]) == (11, 12)
+
+
+def test_mse_hand_values():
+    """The error measure is the mean over a token's channels of the squared
+    difference, one value per token."""
+    assert O.mse(np.array([[1.0, 2.0, 3.0, 4.0]]), np.array([[1.0, 2.0, 3.0, 5.0]])).tolist() == [0.25]
+    got = O.mse(np.array([[0.0, 0.0], [3.0, 4.0]]), np.array([[1.0, 1.0], [0.0, 0.0]]))
+    assert got.tolist() == [1.0, 12.5]
+    # a quantized row: levels 0, 1, ..., 15 (s = 1); 0.25 goes to level 0
+    y = np.array([[0.0, 0.25, 15.0]])
+    q, s, z = O.quant_asym(y)
+    assert q.tolist() == [[0, 0, 15]]
+    assert O.mse(y, O.dequant(q, s, z)).tolist() == [0.0625 / 3]
 
 
 def test_pack_unpack_roundtrip_and_nibble_order():
