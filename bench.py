@@ -16,6 +16,13 @@ The inputs are copied to several device buffers whose total exceeds the
 256 MiB last-level (MALL) cache, and the steps cycle through them, so every
 step reads its input from HBM.
 
+Before the headline steps, three auxiliary legs run on the same buffers, each
+with its own warm-up: a traffic-ceiling kernel that moves the same bytes per
+token with no arithmetic, the d-vector entry point signrot_rotate_quant_int4,
+and the integer zero-point variant.  The line also reports per-launch
+percentiles, the quantization MSE of the GPU's own outputs, and the
+decode-sized latency.
+
 Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 --warmup W, --workload W, --no-cpu-baseline, --no-decode (skip the
 decode-latency leg), --pmc-copy (also run plain copies of known size for the
@@ -93,33 +100,28 @@ def algorithmic_bytes_per_token(n: int) -> int:
     return 2 * n + n // 2 + 8
 
 
-def cpu_baseline(bits: np.ndarray, d: np.ndarray, budget_s: float = 12.0) -> dict:
+def cpu_baseline(bits: np.ndarray, d: np.ndarray) -> dict:
     """Time the oracle (numpy float64, as it stands) on a bounded sample of the
-    same workload: as many 64-token chunks as fit in ~budget_s seconds."""
+    same workload: one call over the first tokens of the batch (2048 at
+    n <= 14336, 1024 above), so the oracle builds its column blocks of H once
+    and the float64 product dominates."""
     import oracle as O
 
     try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    try:
         from threadpoolctl import threadpool_info
 
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=cores)
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = cores
-    chunk = 64
-    done = 0
+        threads = os.cpu_count() or 1
+    n = bits.shape[1]
+    tokens = min(bits.shape[0], 2048 if n <= 14336 else 1024)
     t0 = time.perf_counter()
-    while done + chunk <= bits.shape[0]:
-        O.rotate_quant_int4(bits[done:done + chunk], d)
-        done += chunk
-        if time.perf_counter() - t0 > budget_s:
-            break
+    O.rotate_quant_int4(bits[:tokens], d)
     dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} tokens of the same workload (n={bits.shape[1]}), "
-                      f"oracle rotate (float64 blocked dense product) + asymmetric INT4, {dt:.1f} s"}
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the first {tokens} tokens of the same workload (n={n}) in one oracle call: float64 "
+                      f"dense rotation built from column blocks of H (H construction included) + asymmetric "
+                      f"INT4, {dt:.1f} s"}
 
 
 def bench_fold(args, torch, R, W) -> int:
@@ -386,6 +388,63 @@ def decode_latency(R, W, torch, c, sigma, calls: int = 10000) -> dict:
     return out
 
 
+def timed_launches(torch, stream, launch, steps: int) -> dict:
+    """Run launch(i) for i < steps with a HIP event recorded on `stream`
+    before the first and after every launch.  Returns the mean launch time
+    (last event minus first, over steps) and the 10th / 50th / 90th
+    percentiles of the per-launch intervals, in ms, plus the wall time."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        launch(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    return {"mean_ms": evs[0].elapsed_time(evs[steps]) / steps, "p10_ms": float(np.percentile(per, 10)),
+            "p50_ms": float(np.percentile(per, 50)), "p90_ms": float(np.percentile(per, 90)), "wall_s": wall}
+
+
+def leg(torch, stream, launch, warmup: int, steps: int) -> dict:
+    for i in range(warmup):
+        launch(i)
+    r = timed_launches(torch, stream, launch, steps)
+    r.pop("wall_s")
+    return r
+
+
+def mse_summary(torch, R, x, c, sigma, outlier_tokens, n: int) -> dict:
+    """Quantization MSE of the GPU's own outputs on the first 1024 tokens, in
+    the rotated domain: mean over channels of (y - dequant(codes))^2 with y
+    the kernel's binary32 rotated values, for SignRot (d = sigma * row c of
+    H) and for plain Hadamard (d = all ones), both asymmetric INT4, split into
+    tokens with and without the outlier.  Beside it, the oracle's stored grid
+    (tests/golden/mse_grid.json, written offline by the oracle) for the same
+    law, which also holds the symmetric-INT4 cells."""
+    t = min(1024, x.shape[0])
+    xs = x[:t]
+    out = np.zeros(t, bool)
+    out[outlier_tokens[outlier_tokens < t]] = True
+    res = {"tokens": t, "outlier_tokens": int(out.sum())}
+    ones = torch.ones(n, dtype=torch.int8, device=x.device)
+    for name, call in (("signrot_asym", lambda: R.rotate_quant_int4_outlier(xs, c, sigma, y_out=True)),
+                       ("plain_asym", lambda: R.rotate_quant_int4(xs, ones, y_out=True))):
+        codes, scale, zero, y = call()
+        yh = R.dequant(codes, scale, zero)
+        m = ((y.double() - yh.double()) ** 2).mean(dim=1).cpu().numpy()
+        res[name] = {"outlier": float(m[out].mean()) if out.any() else None,
+                     "no_outlier": float(m[~out].mean()) if (~out).any() else None}
+        del codes, scale, zero, y, yh
+    path = os.path.join(HERE, "tests", "golden", "mse_grid.json")
+    if os.path.exists(path) and n == 14336:
+        with open(path) as f:
+            grid = json.load(f)["workloads"]
+        res["oracle_grid_n14336_t4096"] = grid.get("n14336_t4096")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -443,8 +502,7 @@ def main() -> int:
     stream = torch.cuda.current_stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
     # the step: the calibrated sign vector d = sigma * (row c of H), passed as
-    # (c, sigma); the same computation through the d-vector entry point is
-    # timed after it for reference
+    # (c, sigma)
     calls = []
     for i in range(nsets):
         co, sc, ze = outs[i]
@@ -457,49 +515,48 @@ def main() -> int:
         if st != 0:
             R.check(st, "signrot_rotate_quant_int4_outlier")
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # HIP events over the whole timed region, recorded on the stream the
-    # kernel is launched on; average launch duration = elapsed / steps
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_kernel_ms = ev0.elapsed_time(ev1) / args.steps
-
-    # reference: the same steps through the d-vector entry point
+    # Auxiliary legs first, each with a warm-up of its own: the traffic
+    # ceiling, the d-vector entry point and the integer zero-point variant on
+    # the same buffers.  They also bring the GPU to its steady clock before
+    # the headline step is timed.
     dcalls = [(xs[i].data_ptr(), t, n, n, d.data_ptr(), outs[i][0].data_ptr(), outs[i][1].data_ptr(),
                outs[i][2].data_ptr(), None, sptr) for i in range(nsets)]
-    ev2 = torch.cuda.Event(enable_timing=True)
-    ev3 = torch.cuda.Event(enable_timing=True)
-    dsteps = min(args.steps, 200)
-    ev2.record(stream)
-    for i in range(dsteps):
+
+    def dstep(i):
         st = L.signrot_rotate_quant_int4(*dcalls[i % nsets])
         if st != 0:
             R.check(st, "signrot_rotate_quant_int4")
-    ev3.record(stream)
-    torch.cuda.synchronize()
-    dvec_ms = ev2.elapsed_time(ev3) / dsteps
-    # and through the integer zero-point variant
-    ev2.record(stream)
-    for i in range(dsteps):
+
+    def zstep(i):
         co, sc, ze = outs[i % nsets]
         st = L.signrot_rotate_quant_int4_zint(xs[i % nsets].data_ptr(), t, n, n, c, sigma, co.data_ptr(),
                                              sc.data_ptr(), ze.data_ptr(), sptr)
         if st != 0:
             R.check(st, "signrot_rotate_quant_int4_zint")
-    ev3.record(stream)
+
+    def cstep(i):
+        co, sc, ze = outs[i % nsets]
+        st = L.signrot_stream_ceiling(xs[i % nsets].data_ptr(), t, n, n, co.data_ptr(), sc.data_ptr(),
+                                      ze.data_ptr(), sptr)
+        if st != 0:
+            R.check(st, "signrot_stream_ceiling")
+
+    aux_steps = 200
+    ceiling = leg(torch, stream, cstep, 100, aux_steps)
+    dvec = leg(torch, stream, dstep, 100, aux_steps)
+    zint = leg(torch, stream, zstep, 100, aux_steps)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    zint_ms = ev2.elapsed_time(ev3) / dsteps
+
+    # HIP events on the stream the kernel is launched on, one before the
+    # first timed step and one after every step: the average launch duration
+    # is (last - first) / steps, and the per-launch intervals give the
+    # percentiles.  synchronize() brackets the timed region on both sides.
+    head = timed_launches(torch, stream, step, args.steps)
+    wall = head["wall_s"]
+    avg_kernel_ms = head["mean_ms"]
 
     if args.pmc_copy:
         # plain copies of known size, for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE
@@ -515,6 +572,7 @@ def main() -> int:
     bpt = algorithmic_bytes_per_token(n)
     achieved = bpt * t / (avg_kernel_ms * 1e-3) / 1e9
     kname = R.kernel_name(n)
+    ceiling_gbs = bpt * t / (ceiling["mean_ms"] * 1e-3) / 1e9
     traffic_bytes = measured_traffic(kname, n, t)
     traffic = None if traffic_bytes is None else traffic_bytes / (avg_kernel_ms * 1e-3) / 1e9
     line = {
@@ -537,8 +595,12 @@ def main() -> int:
             "parallelism": "single GPU",
             "kernel": kname,
             "entry_point": "signrot_rotate_quant_int4_outlier (d = sigma * row c of H, from calibration)",
-            "d_vector_entry_point_kernel_avg_ms": dvec_ms,
-            "integer_zero_point_variant_kernel_avg_ms": zint_ms,
+            "d_vector_entry_point_kernel_avg_ms": dvec["mean_ms"],
+            "d_vector_entry_point_launch_ms": dvec,
+            "integer_zero_point_variant_kernel_avg_ms": zint["mean_ms"],
+            "integer_zero_point_variant_launch_ms": zint,
+            "launch_ms": {k: head[k] for k in ("mean_ms", "p10_ms", "p50_ms", "p90_ms")},
+            "aux_legs": f"{aux_steps} launches each after 100 warm-up, run before the headline steps",
             "input_buffer_sets": nsets,
             "hbm_gbs_wall": bpt * tokens_per_s / 1e9,
             "pct_of_peak_hbm_wall": 100.0 * bpt * tokens_per_s / 1e9 / PEAK_HBM_GBS,
@@ -554,8 +616,13 @@ def main() -> int:
             "algorithmic_bytes_per_launch": bpt * t,
             "bytes_per_token": bpt,
             "kernel_avg_ms": avg_kernel_ms,
+            "ceiling": {"kernel": "signrot_stream_ceiling (the path's bytes per token, no arithmetic)",
+                        "achieved": ceiling_gbs, "frac_of_peak": ceiling_gbs / PEAK_HBM_GBS,
+                        "launch_ms": ceiling},
+            "frac_of_ceiling": achieved / ceiling_gbs,
         },
     }
+    line["mse"] = mse_summary(torch, R, x0, c, sigma, meta["outlier_tokens"], n)
     if not args.no_decode and n == 14336:
         line["decode"] = {"workload": "n=14336, 1/4/16 tokens per call, same law; 10^4 calls",
                           "tokens": decode_latency(R, W, torch, c, sigma)}

@@ -48,6 +48,16 @@
  *   - Non-finite inputs, or inputs so large that the rotated values overflow
  *     binary32, give unspecified outputs (no checks on the hot path).
  *   - Calls are reentrant; concurrent calls on different streams are allowed.
+ *   - Device memory the library itself allocates: (1) per device, the sign
+ *     table of an outer factor H_m with m != 28 (and the transposed table for
+ *     the outer-order MFMA kernel), at most 32 KiB each, copied there by the
+ *     first call that needs it (hipMalloc + hipMemcpy) and kept until the
+ *     process ends; a first call made while `stream` is being captured into
+ *     a graph returns SIGNROT_EHIP instead and leaves the capture intact.
+ *     H28 (every width 28 * 2^k) and the Sylvester-only widths with their own
+ *     kernel need no table: H28 travels by value in the kernel arguments.
+ *     (2) Stream-ordered scratch (hipMallocAsync / hipFreeAsync on `stream`),
+ *     named at each call that uses it.  Nothing else.
  */
 #ifndef SIGNROT_H
 #define SIGNROT_H
@@ -88,8 +98,10 @@ int signrot_outer_order(int64_t n);
  *
  * Enqueues its kernels on `stream`, then synchronizes that stream (the host
  * outputs need the result).  Uses a 16-byte stream-ordered scratch buffer
- * (hipMallocAsync / hipFreeAsync).  tokens == 0 -> SIGNROT_EINVAL (there is no
- * channel to find).
+ * (hipMallocAsync / hipFreeAsync).  Unlike the other calls, tokens == 0 ->
+ * SIGNROT_EINVAL: an empty batch has no largest activation, so there is no
+ * channel to find.  t_out is reported in addition to c and M_c so that a
+ * caller can check the argmax against its own data.
  */
 int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
                       int8_t* d_out, int32_t* c_out, int64_t* t_out, float* mc_out,
@@ -171,9 +183,20 @@ int signrot_rotate_quant_int4_zint(const void* x_bf16, int64_t tokens, int64_t n
                                    uint8_t* codes, float* scale, float* zero, void* stream);
 
 /*
- * Dequantization: y_hat[t][j] = scale[t] * (q_j - zero[t]), the level value
- * of each code (mn + q * scale).  codes/scale/zero as produced above; y_hat
- * device [tokens][n] float.  n must be supported.  Asynchronous.
+ * Dequantization (explainer, paragraph on the 4-bit quantizer: a token's 16
+ * levels are spread evenly from its smallest to its largest value, so code q
+ * stands for the level mn + q * scale; paragraph on symmetric versus
+ * asymmetric quantizers: the asymmetric form carries a zero-point):
+ * y_hat[t][j] = scale[t] * (q_j - zero[t]).
+ *
+ *   codes   device, [tokens][n/2] uint8, as signrot_rotate_quant_int4 or
+ *           signrot_rotate_quant_int4_zint writes them.
+ *   scale   device, [tokens] float; zero device, [tokens] float.
+ *   y_hat   device, [tokens][n] float, 8-byte aligned.
+ *
+ * n must be supported (SIGNROT_EUNSUPPORTED_N otherwise); a null pointer or a
+ * misaligned y_hat (tokens > 0) or tokens < 0 -> SIGNROT_EINVAL.  No
+ * allocation.  Asynchronous.
  */
 int signrot_dequant(const uint8_t* codes, const float* scale, const float* zero,
                     int64_t tokens, int64_t n, float* y_hat, void* stream);
@@ -249,6 +272,19 @@ int signrot_int4_linear(const uint8_t* codes, const float* scale, const float* z
  * string), or NULL when the arguments are invalid. */
 const char* signrot_int4_linear_kernel_name(const uint8_t* codes, int64_t tokens, int64_t n, const void* w_bf16,
                                             int64_t ldw, int64_t rows);
+
+/*
+ * Measurement aid, not part of the method: a kernel that moves the bytes the
+ * online path moves per token -- reads the bf16 row (2n bytes), writes n/2
+ * bytes to out [tokens][n/2] and one float each to s0 [tokens] and
+ * s1 [tokens] -- with no arithmetic (each 16-byte input chunk becomes the XOR
+ * of its four words).  Its time is the memory system's ceiling for that
+ * read/write mix at the shape.  n a multiple of 8 in [8, 32768], ld >= n and
+ * a multiple of 8, tokens * n / 8 < 2^32, x 16-byte and out 4-byte aligned.
+ * Asynchronous.
+ */
+int signrot_stream_ceiling(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, uint8_t* out, float* s0,
+                           float* s1, void* stream);
 
 /* Static text for a status code. */
 const char* signrot_strerror(int status);

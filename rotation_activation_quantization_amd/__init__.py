@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_int4_linear.restype = ctypes.c_int
     L.signrot_int4_linear_kernel_name.argtypes = [vp, i64, i64, vp, i64, i64]
     L.signrot_int4_linear_kernel_name.restype = ctypes.c_char_p
+    L.signrot_stream_ceiling.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    L.signrot_stream_ceiling.restype = ctypes.c_int
     L.signrot_strerror.argtypes = [ctypes.c_int]
     L.signrot_strerror.restype = ctypes.c_char_p
     L.signrot_last_error.argtypes = []
@@ -100,6 +102,7 @@ EXPORTED = (
     "signrot_outer_order",
     "signrot_outer_fold",
     "signrot_kernel_name",
+    "signrot_stream_ceiling",
 )
 
 
@@ -316,6 +319,22 @@ def int4_linear_kernel_name(codes, w) -> str | None:
     wptr, rows, n, ld = _linear_operands(codes, w)
     r = lib().signrot_int4_linear_kernel_name(codes.data_ptr(), codes.shape[0], n, wptr, ld, rows)
     return r.decode() if r else None
+
+
+def signrot_stream_ceiling(x, out=None):
+    """The memory-traffic ceiling kernel (a measurement aid: the online path's
+    bytes per token, no arithmetic) on bf16 [T, n] -> (u8 [T, n/2], f32 [T],
+    f32 [T])."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    if out is None:
+        out = (torch.empty((t, n // 2), dtype=torch.uint8, device=x.device),
+               torch.empty(t, dtype=torch.float32, device=x.device),
+               torch.empty(t, dtype=torch.float32, device=x.device))
+    check(lib().signrot_stream_ceiling(ptr, t, n, ld, out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(),
+                                       _stream_of(x)), "signrot_stream_ceiling")
+    return out
 
 
 # short aliases

@@ -26,6 +26,7 @@ SOURCES = [
     "rq_outer_t8.hip",
     "rq_outer_t16.hip",
     "calib_dequant.hip",
+    "ceiling.hip",
     "linear.hip",
     "hadamard28.cpp",
     "outer.cpp",

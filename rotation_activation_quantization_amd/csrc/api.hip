@@ -64,7 +64,7 @@ Shape factor_n(int64_t n) {
   return s;
 }
 
-const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed, int fold) {
+const uint32_t* outer_mask_device(int m, hipError_t* err, hipStream_t stream, bool transposed, int fold) {
   *err = hipSuccess;
   static std::mutex mu;
   static std::vector<std::vector<std::pair<int, uint32_t*>>> per_dev;
@@ -75,6 +75,13 @@ const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed, int f
   const int key = ((m * 16 + fold) * 2) + (transposed ? 1 : 0);
   for (auto& e : per_dev[dev])
     if (e.first == key) return e.second;
+  // the copy below would break a stream capture: refuse instead
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if ((*err = hipStreamIsCapturing(stream, &cap)) != hipSuccess) return nullptr;
+  if (cap != hipStreamCaptureStatusNone) {
+    *err = hipErrorStreamCaptureUnsupported;
+    return nullptr;
+  }
   std::vector<uint32_t> mask;
   if (fold > 0) {
     const OuterTable* t = outer_table_folded(m, fold);
@@ -139,11 +146,11 @@ RqPlan rq_plan_for(const Shape& sh) {
 RqKernel rq_kernel_for(const Shape& sh) { return rq_plan_for(sh).kind; }
 
 // Fills the outer-factor fields of a (the device sign tables it needs); with
-// a fold, also the outer order and Sylvester exponent the kernel sees.  The
-// fast kernels take H28 by value (h28mask) and read no table, so their calls
-// never allocate one: after the first call on a device, a captured call makes
-// no runtime allocation.
-hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
+// a fold, also the outer order and Sylvester exponent the kernel sees.  Every
+// kernel takes H28 by value (h28mask) and reads no table for m = 28, so those
+// widths never allocate one; other outer orders read a per-device table that
+// is copied there on a device's first call and kept.
+hipError_t set_outer_tables(RqArgs& a, const Shape& sh, hipStream_t s) {
   hipError_t he = hipSuccess;
   const RqPlan p = rq_plan_for(sh);
   a.m = sh.m << p.fold;
@@ -151,9 +158,9 @@ hipError_t set_outer_tables(RqArgs& a, const Shape& sh) {
   a.hw = (a.m + 31) / 32;
   a.hm = nullptr;
   a.hmt = nullptr;
-  if (a.m > 1 && p.kind != RqKernel::kFast) {
-    if (!(a.hm = outer_mask_device(sh.m, &he, false, p.fold))) return he;
-    if (p.kind == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, true, p.fold))) return he;
+  if (a.m > 1 && a.m != 28 && p.kind != RqKernel::kFast) {
+    if (!(a.hm = outer_mask_device(sh.m, &he, s, false, p.fold))) return he;
+    if (p.kind == RqKernel::kOuter && !(a.hmt = outer_mask_device(sh.m, &he, s, true, p.fold))) return he;
   }
   return hipSuccess;
 }
@@ -326,7 +333,7 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    const hipError_t he = set_outer_tables(a, sh);
+    const hipError_t he = set_outer_tables(a, sh, static_cast<hipStream_t>(stream));
     if (he != hipSuccess) return fail_hip(he, "outer Hadamard factor table");
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -377,7 +384,7 @@ int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int
   a.zint = zint;
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    const hipError_t he = set_outer_tables(a, sh);
+    const hipError_t he = set_outer_tables(a, sh, static_cast<hipStream_t>(stream));
     if (he != hipSuccess) return fail_hip(he, "outer Hadamard factor table");
   }
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -455,7 +462,7 @@ int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld
   a.inv_15sqrt_n = static_cast<float>(1.0 / (15.0 * sqrt(static_cast<double>(n))));
   for (int i = 0; i < 28; ++i) a.h28mask[i] = h28().rowmask[i];
   {
-    const hipError_t he = set_outer_tables(a, sh);
+    const hipError_t he = set_outer_tables(a, sh, static_cast<hipStream_t>(stream));
     if (he != hipSuccess) {
       (void)hipFreeAsync(scratch, s);
       return fail_hip(he, "outer Hadamard factor table");
@@ -541,6 +548,22 @@ const char* signrot_int4_linear_kernel_name(const uint8_t* codes, int64_t tokens
   if (fill_linear(a, codes, nullptr, nullptr, tokens, n, w_bf16, ldw, nullptr, rows, nullptr) != SIGNROT_OK)
     return nullptr;
   return int4_linear_name(a);
+}
+
+int signrot_stream_ceiling(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, uint8_t* out, float* s0,
+                           float* s1, void* stream) {
+  g_last_error[0] = '\0';
+  if (tokens < 0) return fail_einval("tokens < 0");
+  if (n < 8 || n > 32768 || (n & 7)) return fail_einval("n must be a multiple of 8 in [8, 32768]");
+  if (ld < n || (ld & 7)) return fail_einval("ld must be >= n and a multiple of 8");
+  if (tokens == 0) return SIGNROT_OK;
+  if (tokens * (n / 8) >= (int64_t{1} << 32)) return fail_einval("tokens * n / 8 must be < 2^32");
+  if (!x_bf16 || !out || !s0 || !s1) return fail_einval("null device pointer");
+  if (!aligned16(x_bf16) || (reinterpret_cast<uintptr_t>(out) & 3u)) return fail_einval("x must be 16-byte and out 4-byte aligned");
+  hipError_t e = launch_stream_ceiling(static_cast<const uint16_t*>(x_bf16), tokens, static_cast<int>(n), ld, out, s0,
+                                       s1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e, "stream_ceiling launch");
+  return SIGNROT_OK;
 }
 
 }  // extern "C"

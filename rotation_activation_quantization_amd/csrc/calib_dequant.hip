@@ -52,33 +52,40 @@ __global__ __launch_bounds__(kCalThreads) void cal_argmax_kernel(const uint16_t*
   }
 }
 
+// Sign bit (1 = negative) of entry j of row c of H = H_m (x) H_{2^k}: the
+// Sylvester part from the parity of c & j over the low k bits, the outer part
+// from the order-28 row masks passed by value (m = 28) or from the device mask
+// table of H_m (other m > 1).
+__device__ __forceinline__ uint32_t row_negbit(int c, int j, int k, int m, int hw, const uint32_t* hm,
+                                               const H28Masks& h28) {
+  const int bmask = (1 << k) - 1;
+  uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
+  if (m == 28) bit ^= (h28.m[c >> k] >> (j >> k)) & 1u;
+  else if (m > 1) bit ^= (hm[(c >> k) * hw + ((j >> k) >> 5)] >> ((j >> k) & 31)) & 1u;
+  return bit;
+}
+
 // Fills d[j] = sigma * H[c][j]; also records the bf16 bits of M_c in scratch[1].
 __global__ void cal_fill_kernel(const uint16_t* x, int64_t ld, int n, int k, int m, int hw,
-                                const uint32_t* hm, unsigned long long* scratch, int8_t* d) {
+                                const uint32_t* hm, H28Masks h28, unsigned long long* scratch, int8_t* d) {
   const unsigned long long key = scratch[0];
   const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
   const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
   const uint32_t mbits = x[t * ld + c];
   // sigma = sign(M_c), with sign(+-0) = +1
   const uint32_t neg = ((mbits & 0x7fffu) != 0u) && ((mbits & 0x8000u) != 0u);
-  const int bmask = (1 << k) - 1;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-    if (m > 1) bit ^= (hm[(c >> k) * hw + ((j >> k) >> 5)] >> ((j >> k) & 31)) & 1u;
-    d[j] = (bit ^ neg) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
-  }
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x)
+    d[j] = (row_negbit(c, j, k, m, hw, hm, h28) ^ neg) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
   if (blockIdx.x == 0 && threadIdx.x == 0) scratch[1] = mbits;
 }
 
 // d[j] = sigma * H[c][j] for a given (c, sigma): the same entries as the
 // calibration fill.
-__global__ void sign_fill_kernel(int n, int k, int m, int hw, const uint32_t* hm, int c, int neg, int8_t* d) {
-  const int bmask = (1 << k) - 1;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-    if (m > 1) bit ^= (hm[(c >> k) * hw + ((j >> k) >> 5)] >> ((j >> k) & 31)) & 1u;
-    d[j] = (bit ^ static_cast<uint32_t>(neg)) ? static_cast<int8_t>(-1) : static_cast<int8_t>(1);
-  }
+__global__ void sign_fill_kernel(int n, int k, int m, int hw, const uint32_t* hm, H28Masks h28, int c, int neg,
+                                 int8_t* d) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x)
+    d[j] = (row_negbit(c, j, k, m, hw, hm, h28) ^ static_cast<uint32_t>(neg)) ? static_cast<int8_t>(-1)
+                                                                             : static_cast<int8_t>(1);
 }
 
 // y[t][j] = scale[t] * (q - zero[t]); one thread per code byte.
@@ -114,10 +121,10 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t* hm = nullptr;
-  if (sh.m > 1 && !(hm = outer_mask_device(sh.m, &e))) return e;
+  if (sh.m > 1 && sh.m != 28 && !(hm = outer_mask_device(sh.m, &e, s))) return e;
   const int fill_blocks = (sh.n + 255) / 256;
   hipLaunchKernelGGL(cal_fill_kernel, dim3(fill_blocks), dim3(256), 0, s, x, ld, sh.n, sh.k, sh.m,
-                     (sh.m + 31) / 32, hm, scratch, d_out);
+                     (sh.m + 31) / 32, hm, h28_masks(), scratch, d_out);
   return hipGetLastError();
 }
 
@@ -136,10 +143,10 @@ hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float*
 hipError_t launch_sign_fill(const Shape& sh, int c, int neg, int8_t* d, hipStream_t s) {
   hipError_t e = hipSuccess;
   const uint32_t* hm = nullptr;
-  if (sh.m > 1 && !(hm = outer_mask_device(sh.m, &e))) return e;
+  if (sh.m > 1 && sh.m != 28 && !(hm = outer_mask_device(sh.m, &e, s))) return e;
   const int blocks = (sh.n + 255) / 256;
-  hipLaunchKernelGGL(sign_fill_kernel, dim3(blocks), dim3(256), 0, s, sh.n, sh.k, sh.m, (sh.m + 31) / 32, hm, c, neg,
-                     d);
+  hipLaunchKernelGGL(sign_fill_kernel, dim3(blocks), dim3(256), 0, s, sh.n, sh.k, sh.m, (sh.m + 31) / 32, hm,
+                     h28_masks(), c, neg, d);
   return hipGetLastError();
 }
 

@@ -16,12 +16,19 @@ __device__ __forceinline__ uint32_t outer_negbit(const uint32_t* hm, int words, 
   return (hm[r * words + (col >> 5)] >> (col & 31)) & 1u;
 }
 
+// Sign bit of H_m[r][col] for the outer factor of a: the order-28 row masks
+// passed by value (m = 28), else the device mask table.
+__device__ __forceinline__ uint32_t args_outer_negbit(const RqArgs& a, int r, int col) {
+  if (a.m == 28) return (a.h28mask[r] >> col) & 1u;
+  return outer_negbit(a.hm, a.hw, r, col);
+}
+
 // Sign bit (1 = negative) of entry j of row c of H, H = H_m (x) H_{2^k} or
 // the Sylvester matrix alone (m = 1).
 __device__ __forceinline__ uint32_t hrow_negbit(const RqArgs& a, int c, int j) {
   const int bmask = (1 << a.k) - 1;
   uint32_t bit = __popc(static_cast<uint32_t>(c & j & bmask)) & 1u;
-  if (a.m > 1) bit ^= outer_negbit(a.hm, a.hw, c >> a.k, j >> a.k);
+  if (a.m > 1) bit ^= args_outer_negbit(a, c >> a.k, j >> a.k);
   return bit;
 }
 
@@ -50,10 +57,10 @@ __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, in
   const uint32_t d0 = dbit(0);
   if (a.m > 1) {
     for (int r = tid; r < a.m; r += blockDim.x) {
-      const uint32_t r0 = outer_negbit(a.hm, a.hw, r, 0);
+      const uint32_t r0 = args_outer_negbit(a, r, 0);
       int ok = 1;
       for (int ap = 0; ap < a.m && ok; ++ap)
-        ok = ((dbit(ap << a.k) ^ d0) == (outer_negbit(a.hm, a.hw, r, ap) ^ r0));
+        ok = ((dbit(ap << a.k) ^ d0) == (args_outer_negbit(a, r, ap) ^ r0));
       if (ok) sh_scratch[3] = r;  // at most one row matches
     }
   }
@@ -66,7 +73,7 @@ __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, in
     const int ca = found ? sh_scratch[3] : 0;
     const int c = (ca << a.k) | cb;
     // sigma: d_0 = sigma * H[c][0]
-    const uint32_t neg = d0 ^ (a.m > 1 ? outer_negbit(a.hm, a.hw, ca, 0) : 0u);
+    const uint32_t neg = d0 ^ (a.m > 1 ? args_outer_negbit(a, ca, 0) : 0u);
     sh_scratch[0] = found;
     sh_scratch[1] = c;
     sh_scratch[2] = static_cast<int>(neg);

@@ -79,4 +79,10 @@ const H28Table& h28() {
   return table;
 }
 
+H28Masks h28_masks() {
+  H28Masks r;
+  for (int i = 0; i < 28; ++i) r.m[i] = h28().rowmask[i];
+  return r;
+}
+
 }  // namespace signrot

@@ -40,10 +40,14 @@ const OuterTable* outer_table(int m);
 // read with j Sylvester index bits moved into the outer index.
 const OuterTable* outer_table_folded(int m, int j);
 // The mask table of H_m on the current device: copied there on first use
-// (hipMalloc + hipMemcpy, not capturable) and kept until the process ends.
-// nullptr (with *err set) on failure.  transposed: the table of H_m^T;
+// (hipMalloc + hipMemcpy) and kept until the process ends, at most 32 KiB per
+// table.  The first use cannot be captured into a graph: when `stream` is
+// capturing and the table is not there yet, this returns nullptr with
+// *err = hipErrorStreamCaptureUnsupported and leaves the capture intact.
+// nullptr (with *err set) on any failure.  transposed: the table of H_m^T;
 // fold: of H_m (x) Syl_{2^fold} (outer_table_folded).
-const uint32_t* outer_mask_device(int m, hipError_t* err, bool transposed = false, int fold = 0);
+const uint32_t* outer_mask_device(int m, hipError_t* err, hipStream_t stream, bool transposed = false,
+                                  int fold = 0);
 
 // The library's order-28 Hadamard matrix (Paley construction I over GF(27)),
 // built once on the host.  rowmask[a] has bit a' set iff H28[a][a'] == -1.
@@ -57,6 +61,7 @@ const H28Table& h28();
 struct H28Masks {
   uint32_t m[28];
 };
+H28Masks h28_masks();
 
 // Everything a rotate+quant kernel needs, passed by value as the kernel
 // argument block.
@@ -103,6 +108,11 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const
 hipError_t launch_sign_fill(const Shape& sh, int c, int neg, int8_t* d, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float* zero,
                           int64_t tokens, int n, float* y, hipStream_t s);
+
+// The memory-traffic ceiling kernel (same bytes per token as the rotate
+// kernels, no arithmetic): x [tokens][ld] bf16, n % 8 == 0.
+hipError_t launch_stream_ceiling(const uint16_t* x, int64_t tokens, int n, int64_t ld, uint8_t* out, float* s0,
+                                 float* s1, hipStream_t s);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

@@ -85,10 +85,14 @@ __device__ __forceinline__ uint32_t quad_slot(uint32_t q) {
   return 16u * u + ((q >> S::LG) ^ (u * S::SWZ));
 }
 
-template <int KA, int KB, bool GENERAL, bool YOUT, bool ZINT = false>
+// MAYBE_GENERAL: d arrived as a vector and may lack the calibrated form; the
+// body then takes `general` (a wave-uniform flag) at run time, so that both
+// cases share one register allocation.  Without it d is given as (c, sigma).
+template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false>
 __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbits, const uint32_t* h28,
                              const DForm& form, float* red, float* xcl) {
   using S = FastShape<KA, KB>;
+  const bool general = MAYBE_GENERAL && __builtin_amdgcn_readfirstlane(form.structured) == 0;
   constexpr int NT = S::NT;
   constexpr int NV = S::NV;
   constexpr bool kLateStage = (KA == 56);
@@ -98,13 +102,13 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int g = lane >> 4;
   const int nl = lane & 15;
 
-  const int c = GENERAL ? 0 : __builtin_amdgcn_readfirstlane(form.c);
+  const int c = general ? 0 : __builtin_amdgcn_readfirstlane(form.c);
   const int ca = c >> KB;
   const int cb = c & ((1 << KB) - 1);
   const int cbb = cb & 3;
   const int cbq_lo = (cb >> 2) & (NT - 1);
   const int cbq_hi = cb >> (2 + S::LG);
-  const int sig = (!GENERAL && form.neg) ? -1 : 1;
+  const int sig = (!general && __builtin_amdgcn_readfirstlane(form.neg)) ? -1 : 1;
 
   // Staging: chunk unit s = w + W i (i < CPT) of 64 chunks; lane L takes the
   // a-row of parity L & 1 and chunk index e = L >> 1 inside the unit.  With
@@ -144,10 +148,14 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     }
   };
   u32x4_t st[S::CPT];
+  // Row loads through a buffer resource on the row (scalar base, the
+  // wave-uniform unit offset as the scalar offset, the lane offset gl), so no
+  // per-lane 64-bit address is kept across the loop.
   auto load_row = [&](int64_t r) {
-    const uint8_t* rowp = reinterpret_cast<const uint8_t*>(a.x + r * a.ld);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.x + r * a.ld, 2u * S::N);
 #pragma unroll
-    for (int i = 0; i < S::CPT; ++i) st[i] = *reinterpret_cast<const u32x4_t*>(rowp + unit_g(i) + gl);
+    for (int i = 0; i < S::CPT; ++i)
+      st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, gl, unit_g(i), 0));
   };
   // The first row's loads go out before the weights are built (all but the
   // 56-row shape, whose registers are short), so their latency overlaps the
@@ -191,7 +199,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 
   // The thread and chunk that hold x_c (structured d only).
   int xc_wave = -1, xc_lane = 0, xc_i = 0, xc_e = 0;
-  if (!GENERAL) {
+  if (!general) {
     const int chunk = c >> 3;
     const int arow = chunk / S::CR, j = chunk % S::CR;
     const int p = arow >> 1;
@@ -208,12 +216,12 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     xc_lane = 2 * e + (arow & 1);
     xc_e = c & 7;
   }
-  const bool xc_thread = !GENERAL && w == xc_wave && lane == xc_lane;
+  const bool xc_thread = !general && w == xc_wave && lane == xc_lane;
 
   const int ap = 4 * w + g;                      // this lane's output row a'
   const int outm = lane_perm(nl);
   const int chan0 = (ap << KB) + 4 * NT * outm;  // first of this lane's channels
-  const uint32_t dword = GENERAL ? (dbits[chan0 >> 5] >> (chan0 & 31)) : 0u;
+  const uint32_t dword = general ? (dbits[chan0 >> 5] >> (chan0 & 31)) : 0u;
 
   const int64_t tokens = a.tokens;
   const int64_t grid = gridDim.x;
@@ -319,10 +327,14 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     dpp_stage<NV>(v, gdpp1, 1);
     dpp_stage<NV>(v, gdpp2, 2);
     dpp_stage<NV>(v, gdpp3, 3);
-    if (GENERAL) {
+    if (general) {
+      // re-derived every row (an opaque copy), so the compiler does not keep
+      // NV shifted masks live across the loop
+      uint32_t dw = dword;
+      asm volatile("" : "+v"(dw));
 #pragma unroll
       for (int e = 0; e < NV; ++e) {
-        const uint32_t sbit = (dword << (31 - e)) & 0x80000000u;
+        const uint32_t sbit = (dw << (31 - e)) & 0x80000000u;
         v[e] = __uint_as_float(__float_as_uint(v[e]) ^ sbit);
       }
     }
@@ -344,7 +356,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     }
     // x_c of this row, read before the barrier: the previous barrier published
     // it, and its slot is next written (for the row after next) after this one
-    const float xc = GENERAL ? 0.0f : xcl[par];
+    const float xc = general ? 0.0f : xcl[par];
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < S::kWaves; q += 4) {
@@ -396,13 +408,14 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       }
       q[u] = ev | (od << 4);
     }
-    uint8_t* cp = a.codes + row * static_cast<int64_t>(S::N / 2) + chan0 / 2;
+    const __amdgpu_buffer_rsrc_t cs = buffer_rsrc(a.codes + row * static_cast<int64_t>(S::N / 2), S::N / 2);
+    const uint32_t coff = static_cast<uint32_t>(chan0 / 2);
     if constexpr (NT == 8) {
-      *reinterpret_cast<u32x4_t*>(cp) = u32x4_t{q[0], q[1], q[2], q[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0, 0);
     } else if constexpr (NT == 4) {
-      *reinterpret_cast<uint2*>(cp) = make_uint2(q[0], q[1]);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q[0], q[1]}, cs, coff, 0, 0);
     } else {
-      *reinterpret_cast<uint32_t*>(cp) = q[0];
+      __builtin_amdgcn_raw_buffer_store_b32(q[0], cs, coff, 0, 0);
     }
     if (YOUT) {
       float* yp = a.yout + row * static_cast<int64_t>(S::N) + chan0;
@@ -423,7 +436,8 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   wait_vmcnt<0>();
 }
 
-template <int KA, int KB, bool YOUT, bool ZINT = false>
+// DVEC: d is a vector (its form is decided here); otherwise (c, sigma) given.
+template <int KA, int KB, bool DVEC, bool YOUT, bool ZINT = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void rq_fast_kernel(RqArgs a) {
   using S = FastShape<KA, KB>;
@@ -444,7 +458,7 @@ void rq_fast_kernel(RqArgs a) {
     }
   }
   DForm form;
-  if (a.form_given) {
+  if constexpr (!DVEC) {
     // d = sigma * (row c of H) by construction: nothing to read or decode
     __syncthreads();
     form = DForm{1, a.form_c, a.form_neg};
@@ -453,13 +467,7 @@ void rq_fast_kernel(RqArgs a) {
     __syncthreads();
     form = decode_d_form_fast(a, dbits, h28_lds, scratch);
   }
-  if constexpr (ZINT) {
-    // only with d given as (c, sigma): always the structured form
-    rq_fast_body<KA, KB, false, YOUT, true>(a, lds, dbits, h28_lds, form, red, xcl);
-  } else {
-    if (form.structured) rq_fast_body<KA, KB, false, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
-    else rq_fast_body<KA, KB, true, YOUT>(a, lds, dbits, h28_lds, form, red, xcl);
-  }
+  rq_fast_body<KA, KB, DVEC, YOUT, ZINT>(a, lds, dbits, h28_lds, form, red, xcl);
 }
 
 template <int KA, int KB>
@@ -471,7 +479,7 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
   int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, rq_fast_kernel<KA, KB, false>, S::kThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, rq_fast_kernel<KA, KB, true, false>, S::kThreads, 0) !=
             hipSuccess ||
         blocks < 1)
       blocks = 1;
@@ -482,12 +490,12 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
   if (grid > a.tokens) grid = a.tokens;
   const dim3 blocks(static_cast<unsigned>(grid));
   const dim3 threads(static_cast<unsigned>(S::kThreads));
-  if (a.zint)
-    rq_fast_kernel<KA, KB, false, true><<<blocks, threads, 0, stream>>>(a);  // no y_out with zint
-  else if (a.yout)
-    rq_fast_kernel<KA, KB, true><<<blocks, threads, 0, stream>>>(a);
+  if (a.zint)  // only with d given as (c, sigma), and no y_out
+    rq_fast_kernel<KA, KB, false, false, true><<<blocks, threads, 0, stream>>>(a);
+  else if (a.form_given)
+    (a.yout ? rq_fast_kernel<KA, KB, false, true> : rq_fast_kernel<KA, KB, false, false>)<<<blocks, threads, 0, stream>>>(a);
   else
-    rq_fast_kernel<KA, KB, false><<<blocks, threads, 0, stream>>>(a);
+    (a.yout ? rq_fast_kernel<KA, KB, true, true> : rq_fast_kernel<KA, KB, true, false>)<<<blocks, threads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -130,11 +130,14 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
     const int ap = 16 * mt + nl;
     const bool ok = mt < mtiles && ap < m;
     uint32_t flip = 0u;
-    if (!GENERAL && ok)
-      flip = ((a.hm[ca * a.hw + (ap >> 5)] >> (ap & 31)) & 1u) ^ static_cast<uint32_t>(form.neg);
+    if (!GENERAL && ok) flip = args_outer_negbit(a, ca, ap) ^ static_cast<uint32_t>(form.neg);
+    // order 28 (KC = 1): the column a' of H28 gathered from the row masks
+    uint32_t col28 = 0u;
+    if (m == 28 && ok)
+      for (int r = 0; r < 28; ++r) col28 |= ((a.h28mask[r] >> ap) & 1u) << r;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const uint32_t word = ok ? a.hmt[ap * a.hw + kc] : 0u;
+      const uint32_t word = !ok ? 0u : (m == 28 ? col28 : a.hmt[ap * a.hw + kc]);
       const uint32_t bits = (word >> (8 * g4)) & 0xffu;
       bf16x8_t v;
 #pragma unroll

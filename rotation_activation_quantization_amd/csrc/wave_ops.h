@@ -217,6 +217,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// Buffer resource over `bytes` bytes from a wave-uniform base (raw access,
+// no stride).  Loads and stores through it take the base from scalar
+// registers and a 32-bit per-lane offset, so no per-lane 64-bit address is
+// kept or recomputed per row; accesses beyond `bytes` read 0 and write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
 
 }  // namespace wave
 }  // namespace signrot

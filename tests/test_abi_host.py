@@ -139,6 +139,21 @@ def test_dequant_argument_errors(L):
     assert dq(t=0, c=None, s=None, z=None, y=None) == R.SIGNROT_OK
 
 
+def test_stream_ceiling_argument_errors(L):
+    def sc(x=FAKE, t=3, n=4096, ld=4096, o=FAKE, a=FAKE, b=FAKE):
+        return L.signrot_stream_ceiling(x, t, n, ld, o, a, b, None)
+
+    assert sc(n=12) == R.SIGNROT_EINVAL
+    assert sc(n=32776) == R.SIGNROT_EINVAL
+    assert sc(ld=4095) == R.SIGNROT_EINVAL
+    assert sc(t=-1) == R.SIGNROT_EINVAL
+    assert sc(x=None) == R.SIGNROT_EINVAL
+    assert sc(x=FAKE + 8) == R.SIGNROT_EINVAL
+    assert sc(o=FAKE + 2) == R.SIGNROT_EINVAL
+    assert sc(t=1 << 22, n=8192) == R.SIGNROT_EINVAL
+    assert sc(t=0, x=None, o=None, a=None, b=None) == R.SIGNROT_OK
+
+
 def test_debug_h28_null(L):
     assert L.signrot_debug_h28(None) == R.SIGNROT_EINVAL
 

@@ -84,3 +84,21 @@ def test_concurrent_calls_on_separate_streams():
     for outs in results.values():
         for o in outs:
             assert all(torch.equal(a, b) for a, b in zip(o, want))
+
+
+@pytest.mark.parametrize("n,t", [(14336, 37), (28672, 5), (8, 3), (4104, 9)])
+def test_stream_ceiling_moves_every_byte(n, t):
+    """The traffic-ceiling kernel (a measurement aid) reads every input chunk
+    and writes every output word: out word j of a row is the XOR of the four
+    words of 16-byte input chunk j; s0/s1 hold the row's first two words."""
+    say(f"[gpu] stream ceiling n={n} T={t}")
+    ld = n + 8
+    bits = W.random_rows(t, ld, seed=n, scale=3.0)
+    x = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)[:, :n]
+    out, s0, s1 = R.signrot_stream_ceiling(x)
+    torch.cuda.synchronize()
+    words = bits[:, :n].copy().view(np.uint32).reshape(t, n // 8, 4)
+    want = words[:, :, 0] ^ words[:, :, 1] ^ words[:, :, 2] ^ words[:, :, 3]
+    assert np.array_equal(out.cpu().numpy().view(np.uint32).reshape(t, n // 8), want)
+    assert np.array_equal(s0.cpu().numpy().view(np.uint32), words[:, 0, 0])
+    assert np.array_equal(s1.cpu().numpy().view(np.uint32), words[:, 0, 1])
