@@ -108,6 +108,24 @@ int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
                       void* stream);
 
 /*
+ * signrot_calibrate without any allocation, for callers that cannot allocate
+ * device memory (tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, outputs and argument errors as signrot_calibrate.  The 16-byte
+ * argmax record lives in a static device array of the library (one per GPU,
+ * kept until the process ends; its address is looked up once per device)
+ * instead of a stream-ordered allocation; each call clears it first.  The
+ * record's size does not depend on the input, so no input is too large for
+ * it.  Only widths whose Hadamard factors need no device table are taken,
+ * n = 2^k and n = 28 * 2^k; any other supported n -> SIGNROT_EUNSUPPORTED_N
+ * (use signrot_calibrate).  Calls that overlap on one GPU (several streams or
+ * threads) race on the shared record: serialize them.  Synchronizes `stream`
+ * before returning, as signrot_calibrate does.
+ */
+int signrot_calibrate_noalloc(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
+                              int8_t* d_out, int32_t* c_out, int64_t* t_out, float* mc_out,
+                              void* stream);
+
+/*
  * The online path: y = (x . H / sqrt(n)) (.) d, then per-token asymmetric
  * INT4 (explainer, paragraphs on rotation, on the sign adjustment and on the
  * quantizer).  Per token, with mn = min_j y_j and mx = max_j y_j:

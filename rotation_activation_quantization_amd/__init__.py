@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_supported_n.restype = ctypes.c_int
     L.signrot_calibrate.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
     L.signrot_calibrate.restype = ctypes.c_int
+    L.signrot_calibrate_noalloc.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.signrot_calibrate_noalloc.restype = ctypes.c_int
     L.signrot_rotate_quant_int4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
     L.signrot_rotate_quant_int4.restype = ctypes.c_int
     L.signrot_rotate_quant_int4_outlier.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
@@ -86,6 +88,7 @@ def lib() -> ctypes.CDLL:
 EXPORTED = (
     "signrot_supported_n",
     "signrot_calibrate",
+    "signrot_calibrate_noalloc",
     "signrot_rotate_quant_int4",
     "signrot_rotate_quant_int4_outlier",
     "signrot_rotate_quant_int4_zint",
@@ -186,6 +189,22 @@ def signrot_calibrate(x):
     check(lib().signrot_calibrate(ptr, t, n, ld, d.data_ptr(), ctypes.addressof(c), ctypes.addressof(tt),
                                   ctypes.addressof(m), _stream_of(x)), "signrot_calibrate")
     return d, c.value, tt.value, m.value
+
+
+def signrot_calibrate_noalloc(x, d_out):
+    """signrot_calibrate into a caller-provided d (int8 [n] on the device),
+    without any allocation in the library -> (c, t, M_c)."""
+    import torch
+
+    ptr, t, n, ld = _rows(x)
+    if d_out.dtype != torch.int8 or d_out.numel() != n or not d_out.is_contiguous():
+        raise ValueError("d_out must be a contiguous int8 tensor of n entries")
+    c = ctypes.c_int32()
+    tt = ctypes.c_int64()
+    m = ctypes.c_float()
+    check(lib().signrot_calibrate_noalloc(ptr, t, n, ld, d_out.data_ptr(), ctypes.addressof(c), ctypes.addressof(tt),
+                                          ctypes.addressof(m), _stream_of(x)), "signrot_calibrate_noalloc")
+    return c.value, tt.value, m.value
 
 
 def signrot_rotate_quant_int4(x, d, y_out: bool = False, out=None):

@@ -262,10 +262,10 @@ const char* signrot_kernel_name(int64_t n) {
   }
 }
 
-int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
-                      int32_t* c_out, int64_t* t_out, float* mc_out, void* stream) {
-  g_last_error[0] = '\0';
-  const Shape sh = factor_n(n);
+}  // extern "C"
+
+namespace {
+int calibrate_check(const Shape& sh, const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, const int8_t* d_out) {
   if (!sh.ok) {
     set_error("unsupported n=%s", std::to_string(n).c_str());
     return SIGNROT_EUNSUPPORTED_N;
@@ -275,6 +275,31 @@ int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
   if (!x_bf16 || !d_out) return fail_einval("null device pointer");
   if (ld < n) return fail_einval("ld < n");
   if (!aligned16(x_bf16) || (ld & 7)) return fail_einval("x must be 16-byte aligned and ld a multiple of 8");
+  return SIGNROT_OK;
+}
+
+// Decodes the argmax record (already on the host) into the outputs.
+void calibrate_outputs(const unsigned long long host[2], int32_t* c_out, int64_t* t_out, float* mc_out) {
+  const unsigned long long key = host[0];
+  const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
+  const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
+  const uint32_t mbits = static_cast<uint32_t>(host[1]) << 16;
+  float m;
+  memcpy(&m, &mbits, sizeof(m));
+  if (c_out) *c_out = c;
+  if (t_out) *t_out = t;
+  if (mc_out) *mc_out = m;
+}
+}  // namespace
+
+extern "C" {
+
+int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
+                      int32_t* c_out, int64_t* t_out, float* mc_out, void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  const int st = calibrate_check(sh, x_bf16, tokens, n, ld, d_out);
+  if (st != SIGNROT_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   unsigned long long* scratch = nullptr;
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&scratch), 16, s);
@@ -286,15 +311,32 @@ int signrot_calibrate(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld,
   if (e == hipSuccess) e = ef;
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail_hip(e, "calibrate");
-  const unsigned long long key = host[0];
-  const int c = static_cast<int>(0xfffffu - static_cast<uint32_t>((key >> 28) & 0xfffffu));
-  const int64_t t = static_cast<int64_t>(0x0fffffffu - static_cast<uint32_t>(key & 0x0fffffffu));
-  const uint32_t mbits = static_cast<uint32_t>(host[1]) << 16;
-  float m;
-  memcpy(&m, &mbits, sizeof(m));
-  if (c_out) *c_out = c;
-  if (t_out) *t_out = t;
-  if (mc_out) *mc_out = m;
+  calibrate_outputs(host, c_out, t_out, mc_out);
+  return SIGNROT_OK;
+}
+
+int signrot_calibrate_noalloc(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int8_t* d_out,
+                              int32_t* c_out, int64_t* t_out, float* mc_out, void* stream) {
+  g_last_error[0] = '\0';
+  const Shape sh = factor_n(n);
+  const int st = calibrate_check(sh, x_bf16, tokens, n, ld, d_out);
+  if (st != SIGNROT_OK) return st;
+  if (sh.m != 1 && sh.m != 28) {
+    set_error("n=%s needs the device table of its outer Hadamard factor, which only signrot_calibrate may "
+              "allocate (the allocation-free call takes n = 2^k and n = 28 * 2^k)",
+              std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  unsigned long long* rec = calib_scratch_device(&e);
+  if (!rec) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+  e = launch_calibrate(static_cast<const uint16_t*>(x_bf16), tokens, ld, sh, d_out, rec, s);
+  unsigned long long host[2] = {0ull, 0ull};
+  if (e == hipSuccess) e = hipMemcpyAsync(host, rec, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail_hip(e, "calibrate_noalloc");
+  calibrate_outputs(host, c_out, t_out, mc_out);
   return SIGNROT_OK;
 }
 

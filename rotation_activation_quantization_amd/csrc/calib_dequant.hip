@@ -8,9 +8,21 @@
 //   key = |x| bits (15) << 48 | (2^20 - 1 - j) << 28 | (2^28 - 1 - t),
 // so the unsigned maximum is the largest |x|, then the smallest channel j,
 // then the smallest token t.  bf16 magnitudes order like their bit patterns.
+#include <mutex>
+#include <vector>
+
 #include "device_common.h"
 
 namespace signrot {
+
+// The argmax record of signrot_calibrate_noalloc: key (word 0) and the bf16
+// bits of M_c (word 1), in a file-scope device array instead of a per-call
+// allocation.  Every call on a device reuses that device's copy (cleared by
+// cal_init_kernel at the start of each call); calls that overlap on one
+// device race on it.  Host code never passes the array's name to a kernel:
+// it passes the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned long long scratch[kCalScratchWords];
+
 namespace {
 
 constexpr int kCalThreads = 256;
@@ -126,6 +138,23 @@ hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const
   hipLaunchKernelGGL(cal_fill_kernel, dim3(fill_blocks), dim3(256), 0, s, x, ld, sh.n, sh.k, sh.m,
                      (sh.m + 31) / 32, hm, h28_masks(), scratch, d_out);
   return hipGetLastError();
+}
+
+unsigned long long* calib_scratch_device(hipError_t* err) {
+  static std::mutex mu;
+  static std::vector<unsigned long long*> per_dev;
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev >= static_cast<int>(per_dev.size())) per_dev.resize(dev + 1, nullptr);
+  if (!per_dev[dev]) {
+    unsigned long long* ptr = nullptr;
+    if ((*err = hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch))) != hipSuccess)
+      return nullptr;
+    per_dev[dev] = ptr;
+  }
+  *err = hipSuccess;
+  return per_dev[dev];
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const float* scale, const float* zero, int64_t tokens,

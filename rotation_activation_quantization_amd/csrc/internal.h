@@ -102,6 +102,12 @@ bool rq_outer_supports(int m, int k);
 hipError_t launch_rq_outer(const RqArgs& a, hipStream_t s);
 const char* rq_outer_name();
 
+// The calibration argmax record in static device memory (two 64-bit words:
+// key, M_c bits): its address on the current device, looked up once per
+// device with hipGetSymbolAddress.  nullptr (with *err set) on failure.
+constexpr int kCalScratchWords = 2;
+unsigned long long* calib_scratch_device(hipError_t* err);
+
 hipError_t launch_calibrate(const uint16_t* x, int64_t tokens, int64_t ld, const Shape& sh,
                             int8_t* d_out, unsigned long long* scratch, hipStream_t s);
 // d[j] = sigma * H[c][j] as int8 +-1 (the calibrated form from (c, sigma)).

@@ -128,6 +128,21 @@ def test_calibrate_argument_errors(L):
     assert cal(x=FAKE + 2) == R.SIGNROT_EINVAL
 
 
+def test_calibrate_noalloc_argument_errors(L):
+    def cal(x=FAKE, t=4, n=4096, ld=4096, d=FAKE):
+        return L.signrot_calibrate_noalloc(x, t, n, ld, d, None, None, None, None)
+
+    assert cal(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert cal(n=11008, ld=11008) == R.SIGNROT_EUNSUPPORTED_N  # outer order 344 needs a device table
+    assert b"device table" in L.signrot_last_error()
+    assert cal(t=0) == R.SIGNROT_EINVAL
+    assert cal(t=1 << 28) == R.SIGNROT_EINVAL
+    assert cal(x=None) == R.SIGNROT_EINVAL
+    assert cal(d=None) == R.SIGNROT_EINVAL
+    assert cal(ld=100) == R.SIGNROT_EINVAL
+    assert cal(x=FAKE + 2) == R.SIGNROT_EINVAL
+
+
 def test_dequant_argument_errors(L):
     def dq(c=FAKE, s=FAKE, z=FAKE, t=3, n=4096, y=FAKE):
         return L.signrot_dequant(c, s, z, t, n, y, None)
