@@ -155,7 +155,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.x + r * a.ld, 2u * S::N);
 #pragma unroll
     for (int i = 0; i < S::CPT; ++i)
-      st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, gl, unit_g(i), 0));
+      st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, gl, unit_g(i), kNontemporal));
   };
   // The first row's loads go out before the weights are built (all but the
   // 56-row shape, whose registers are short), so their latency overlaps the
@@ -350,7 +350,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     mx = fmax_raw(mx, v[NV - 1]);
     wave_minmax(mn, mx);
     float* rd = red + 32 * par;  // per-wave min at rd[w], max at rd[16 + w]
-    if (lane == 0) {
+    if (lane == 63) {
       rd[w] = mn;
       rd[16 + w] = mx;
     }
@@ -411,11 +411,11 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     const __amdgpu_buffer_rsrc_t cs = buffer_rsrc(a.codes + row * static_cast<int64_t>(S::N / 2), S::N / 2);
     const uint32_t coff = static_cast<uint32_t>(chan0 / 2);
     if constexpr (NT == 8) {
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0, kNontemporal);
     } else if constexpr (NT == 4) {
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q[0], q[1]}, cs, coff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q[0], q[1]}, cs, coff, 0, kNontemporal);
     } else {
-      __builtin_amdgcn_raw_buffer_store_b32(q[0], cs, coff, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(q[0], cs, coff, 0, kNontemporal);
     }
     if (YOUT) {
       float* yp = a.yout + row * static_cast<int64_t>(S::N) + chan0;

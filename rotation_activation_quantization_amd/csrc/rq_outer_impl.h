@@ -325,7 +325,7 @@ __device__ void rq_outer_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbi
       }
     wave_minmax(mn, mx);
     float* rd = red + 32 * par;  // per-wave min at rd[w], max at rd[16 + w]
-    if (lane == 0) {
+    if (lane == 63) {
       rd[w] = mn;
       rd[16 + w] = mx;
     }

@@ -1,7 +1,7 @@
 // Wave-level building blocks shared by the MFMA rotate+quant kernels (gfx950):
 // operand vector types, the DPP butterfly stages of the 16-point lane
 // transform, in-register butterflies, min/max helpers and wave reductions,
-// and the LDS-only barrier.
+// buffer resources, and the LDS-only barrier.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -146,12 +146,14 @@ __device__ __forceinline__ float fmax_raw(float x, float y) {
   return r;
 }
 
-// Wave-wide min and max, every lane gets the result: DPP inside 16-lane rows,
-// then the gfx950 row swaps across rows and halves.
+// Wave-wide min and max, the result guaranteed in lane 63 (other lanes end
+// with the min / max of a subset of the wave, never below / above the true
+// one): DPP inside 16-lane rows (lane ^ 1, lane ^ 2, mirror in 8, mirror in
+// 16), then the gfx9 row broadcasts (rows 1 and 3 take the last lane of rows
+// 0 and 2; rows 2 and 3 take the last lane of row 1).  Each step is one
+// v_min / v_max with a DPP source; the s_nop cover the VALU-write ->
+// DPP-read hazard of the chained registers.
 __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
-  // inside each 16-lane row: lane ^ 1, lane ^ 2, mirror in 8, mirror in 16,
-  // each step one v_min/v_max with a DPP source; the s_nop cover the
-  // VALU-write -> DPP-read hazard of the chained registers
   asm volatile(
       "s_nop 1\n"
       "v_min_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n"
@@ -165,19 +167,13 @@ __device__ __forceinline__ void wave_minmax(float& mn, float& mx) {
       "s_nop 1\n"
       "v_min_f32_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n"
       "v_max_f32_dpp %1, %1, %1 row_mirror row_mask:0xf bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n"
+      "s_nop 1\n"
+      "v_min_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
+      "v_max_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n"
       : "+v"(mn), "+v"(mx));
-  {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-    auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mn = fmin_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    mx = fmax_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
-  }
-  {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    mn = fmin_raw(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    mx = fmax_raw(__uint_as_float(b[0]), __uint_as_float(b[1]));
-  }
 }
 
 // Quantizer constants of a token from the min and max of its rotated values
@@ -218,6 +214,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// Cache policy of the buffer accesses that touch each byte once (the row
+// loads and the code stores): the gfx940+ nontemporal bit.  Timed on the
+// n = 14336 x 8192 workload it saves about 2% (from the stores).
+constexpr int kNontemporal = 2;
 
 // Buffer resource over `bytes` bytes from a wave-uniform base (raw access,
 // no stride).  Loads and stores through it take the base from scalar
