@@ -52,16 +52,33 @@ struct DForm {
 __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, int* sh_scratch) {
   const int tid = threadIdx.x;
   auto dbit = [&](int j) -> uint32_t { return (dbits[j >> 5] >> (j & 31)) & 1u; };
+  // the normalised first column of every block, d[a' 2^k] ^ d[0], as words
+  __shared__ uint32_t sh_e[kMaxOuter / 32];
   if (tid == 0) sh_scratch[3] = a.m > 1 ? -1 : 0;
-  __syncthreads();
   const uint32_t d0 = dbit(0);
   if (a.m > 1) {
+    for (int wd = tid; wd < a.hw; wd += blockDim.x) {
+      uint32_t word = 0u;
+      for (int b = 0; b < 32; ++b) {
+        const int ap = 32 * wd + b;
+        if (ap < a.m) word |= (dbit(ap << a.k) ^ d0) << b;
+      }
+      sh_e[wd] = word;
+    }
+  }
+  __syncthreads();
+  if (a.m > 1) {
+    // one candidate row per thread, compared a word at a time; the row's
+    // words are read without an early exit, so the loads overlap
     for (int r = tid; r < a.m; r += blockDim.x) {
-      const uint32_t r0 = args_outer_negbit(a, r, 0);
-      int ok = 1;
-      for (int ap = 0; ap < a.m && ok; ++ap)
-        ok = ((dbit(ap << a.k) ^ d0) == (args_outer_negbit(a, r, ap) ^ r0));
-      if (ok) sh_scratch[3] = r;  // at most one row matches
+      const uint32_t r0 = args_outer_negbit(a, r, 0) ? 0xffffffffu : 0u;
+      uint32_t diff = 0u;
+      for (int wd = 0; wd < a.hw; ++wd) {
+        const uint32_t valid = (32 * wd + 32 <= a.m) ? 0xffffffffu : ((1u << (a.m - 32 * wd)) - 1u);
+        const uint32_t row = (a.m == 28) ? a.h28mask[r] : a.hm[r * a.hw + wd];
+        diff |= ((row ^ r0) ^ sh_e[wd]) & valid;
+      }
+      if (diff == 0u) sh_scratch[3] = r;  // at most one row matches
     }
   }
   __syncthreads();
