@@ -48,6 +48,55 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even mantissa), in
+    one rounding step from float64 (no detour through binary32), and return
+    the uint16 bit patterns.  For zero and for finite values inside bf16's
+    normal range (|x| in [2^-126, 2^128)); anything else is rejected."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(~np.isfinite(x)) or np.any((a != 0) & ((a < 2.0 ** -126) | (a >= 2.0 ** 128))):
+        raise ValueError("value outside bf16's normal range")
+    f, e = np.frexp(x)  # x = f * 2^e, 0.5 <= |f| < 1: bf16 keeps 8 significant bits
+    q = np.rint(f * 256.0)  # round half to even on the 8-bit significand
+    r = np.ldexp(q, e - 8)  # exactly representable in bf16 (or 2^128 after a carry: rejected above)
+    return (r.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# The producer of the down-projection input  (explainer, paragraph on the
+# down-projection: the gated nonlinearity sits between the up/gate
+# projections and the down-projection, which is why the rotation there has
+# to run online).  READING: the gated unit is SwiGLU, x = SiLU(gate) * up
+# with SiLU(z) = z / (1 + e^-z), evaluated in float64 and stored as bf16
+# (nearest, ties to even) -- what a bf16 model hands to the down-projection.
+# ---------------------------------------------------------------------------
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)), float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_bf16(gate_bits: np.ndarray, up_bits: np.ndarray) -> np.ndarray:
+    """x = bf16(SiLU(gate) * up) from bf16 gate and up (bit patterns [T, n]),
+    the product taken in float64 and rounded once to bf16.  uint16 bits."""
+    return f64_to_bf16_bits(silu(bf16_bits_to_f64(gate_bits)) * bf16_bits_to_f64(up_bits))
+
+
+def bf16_midpoint_distance(x: np.ndarray) -> np.ndarray:
+    """Distance of each float64 value from the nearest point halfway between
+    two neighbouring bf16 values, relative to |x| (inf for x == 0): the
+    margin by which a rounding to bf16 is decided."""
+    x = np.asarray(x, dtype=np.float64)
+    f, e = np.frexp(x)
+    g = np.abs(f) * 256.0  # significand in [128, 256)
+    d = np.abs(g - np.floor(g) - 0.5) / g
+    return np.where(x == 0, np.inf, d)
+
+
 # ---------------------------------------------------------------------------
 # Hadamard matrices
 # ---------------------------------------------------------------------------

@@ -153,3 +153,32 @@ def random_rows(tokens: int, n: int, seed: int, scale: float = 1.0, outlier: flo
     if outlier and n:
         v[:, seed % n] = np.float32(outlier)
     return f32_to_bf16_bits(v)
+
+
+def swiglu_batch(name: str, tokens: int | None = None, stream: int = 10):
+    """gate and up inputs of a SwiGLU producer (bf16 bits [T, n] each) for the
+    workload's width: gate ~ N(0, 1.5), up ~ N(0, 0.6); in the workload's
+    outlier tokens the outlier channel gets gate ~ U[6, 9] and up = M / gate
+    with M ~ U[m_lo, m_hi], so that SiLU(gate) * up carries the massive value
+    there.  Stream 10 + k of the workload's seed (k = 0 the batch, 1 the
+    calibration batch)."""
+    w = WORKLOADS[name]
+    t = w.tokens if tokens is None else int(tokens)
+    g = rng(w.seed, stream)
+    c, _ = channels(w)
+    has = g.random(t) < w.p_outlier
+    mag = g.uniform(w.m_lo, w.m_hi, size=t)
+    gc = g.uniform(6.0, 9.0, size=t)
+    gate = np.empty((t, w.n), dtype=np.uint16)
+    up = np.empty((t, w.n), dtype=np.uint16)
+    for r0 in range(0, t, _CHUNK):
+        r1 = min(t, r0 + _CHUNK)
+        gv = g.standard_normal((r1 - r0, w.n), dtype=np.float32) * np.float32(1.5)
+        uv = g.standard_normal((r1 - r0, w.n), dtype=np.float32) * np.float32(0.6)
+        sel = has[r0:r1]
+        if sel.any():
+            gv[sel, c] = gc[r0:r1][sel].astype(np.float32)
+            uv[sel, c] = (mag[r0:r1][sel] / gc[r0:r1][sel]).astype(np.float32)
+        gate[r0:r1] = f32_to_bf16_bits(gv)
+        up[r0:r1] = f32_to_bf16_bits(uv)
+    return gate, up, {"channel": c, "outlier_tokens": np.flatnonzero(has)}

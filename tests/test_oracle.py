@@ -805,3 +805,87 @@ def test_zint_degenerate_row():
     y = np.full((1, 8), 2.3)
     q, s, z = O.quant_asym_zint(y, "f64")
     assert s[0] == 1.0 and z[0] == -2.0 and np.all(q == 0)
+
+
+# --------------------------------------------------------------------------
+# SwiGLU producer of the down-projection input (explainer, paragraph on the
+# down-projection: the gated nonlinearity is why the rotation runs online)
+# --------------------------------------------------------------------------
+
+
+def _bf16_value(bits):
+    return float(O.bf16_bits_to_f64(np.array([bits], np.uint16))[0])
+
+
+def test_f64_to_bf16_is_the_nearest_bf16_brute_force():
+    """Against the definition: among the bf16 values next to x, the nearest,
+    and on an exact tie the one with an even last significand bit."""
+    rng = np.random.default_rng(31)
+    xs = np.concatenate([rng.standard_normal(300) * 10.0 ** rng.integers(-8, 9, 300), [1.0, -3.5, 0.0]])
+    got = O.f64_to_bf16_bits(xs)
+    for x, b in zip(xs, got):
+        t = int(np.float32(x).view(np.uint32)) >> 16
+        cands = []
+        for cb in range(t - 2, t + 3):
+            cb &= 0xFFFF
+            v = _bf16_value(cb)
+            if np.isfinite(v) and (v == 0 or np.sign(v) == np.sign(x) or x == 0):
+                cands.append((abs(v - x), cb & 1, v, cb))
+        cands.sort()
+        best = cands[0][0]
+        ties = [c for c in cands if c[0] == best]
+        want = min(ties, key=lambda c: c[1])[2]
+        assert _bf16_value(int(b)) == want, (x, hex(int(b)))
+
+
+def test_f64_to_bf16_ties_go_to_even():
+    """Exact midpoints between neighbouring bf16 values round to the even one."""
+    for lo_bits in (0x3F80, 0x3F81, 0x4120, 0xC2F3, 0x0101):
+        lo, hi = _bf16_value(lo_bits), _bf16_value(lo_bits + 1)
+        mid = (lo + hi) / 2.0
+        b = int(O.f64_to_bf16_bits(np.array([mid]))[0])
+        assert b in (lo_bits, lo_bits + 1) and (b & 1) == 0, hex(b)
+        assert O.bf16_midpoint_distance(np.array([mid]))[0] == 0.0
+
+
+def test_bf16_midpoint_distance_brute_force():
+    rng = np.random.default_rng(37)
+    xs = rng.standard_normal(200) * 10.0 ** rng.integers(-5, 6, 200)
+    d = O.bf16_midpoint_distance(xs)
+    for x, dx in zip(xs, d):
+        t = int(np.float32(x).view(np.uint32)) >> 16
+        vals = [_bf16_value((t + k) & 0xFFFF) for k in range(-2, 3)]
+        mids = [(vals[i] + vals[i + 1]) / 2 for i in range(4)]
+        want = min(abs(x - m) for m in mids) / abs(x)
+        assert abs(dx - want) <= 1e-12 * max(want, 1e-30) + 1e-18, (x, dx, want)
+
+
+def test_silu_closed_forms():
+    """SiLU(0) = 0; SiLU(z) - SiLU(-z) = z s(z) + z s(-z) = z, because
+    s(-z) = 1 - s(z) for the logistic s; SiLU(1) = 1 / (1 + 1/e) =
+    0.7310585786300049."""
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    z = np.linspace(-30, 30, 241)
+    assert np.allclose(O.silu(z) - O.silu(-z), z, rtol=1e-15, atol=1e-13)
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-16
+    assert abs(O.silu(np.array([-1.0]))[0] + 0.2689414213699951) < 1e-16
+    big = O.silu(np.array([50.0, -50.0]))
+    assert big[0] == 50.0 and -1e-19 < big[1] < 0
+
+
+def test_swiglu_bf16_elementwise():
+    """x = bf16(SiLU(gate) * up) element by element, on a tiny hand case and on
+    the seeded producer inputs (the outlier channel carries the massive value)."""
+    g = W.f32_to_bf16_bits(np.array([[0.0, 1.0, -1.0, 8.0]], np.float32))
+    u = W.f32_to_bf16_bits(np.array([[5.0, 2.0, 2.0, 250.0]], np.float32))
+    x = O.bf16_bits_to_f64(O.swiglu_bf16(g, u))[0]
+    assert x[0] == 0.0
+    assert x[1] == _bf16_value(int(O.f64_to_bf16_bits(np.array([2 * 0.7310585786300049]))[0]))
+    assert x[2] == _bf16_value(int(O.f64_to_bf16_bits(np.array([-2 * 0.2689414213699951]))[0]))
+    assert abs(x[3] - 8.0 / (1 + math.exp(-8.0)) * 250.0) <= 2.0 ** -8 * x[3]
+    gate, up, meta = W.swiglu_batch("n14336_t8192", tokens=32)
+    xb = O.bf16_bits_to_f64(O.swiglu_bf16(gate, up))
+    out = meta["outlier_tokens"]
+    assert len(out) > 0
+    assert np.all(np.abs(xb[out, meta["channel"]]) >= 700)
+    assert np.abs(np.delete(xb, meta["channel"], axis=1)).max() < 100
