@@ -27,7 +27,8 @@ Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 --warmup W, --workload W, --no-cpu-baseline, --no-decode (skip the
 decode-latency leg), --pmc-copy (also run plain copies of known size for the
 counter calibration of a rocprofv3 --pmc run); --fold times the offline weight
-fold and --linear the INT4-activation down-projection instead.
+fold, --linear the INT4-activation down-projection and --swiglu the path with
+the SwiGLU producer fused in, instead.
 """
 
 from __future__ import annotations
@@ -281,6 +282,84 @@ def bench_linear(args, torch, R, W) -> int:
     return 0
 
 
+def bench_swiglu(args, torch, R, W) -> int:
+    """The online path with the SwiGLU producer fused in, on the n = 14336
+    law at 8192 tokens: gate and up bf16 [8192, 14336] (seeded synthetic,
+    the massive channel in 20 % of tokens), d calibrated on x of a 256-token
+    calibration batch.  One step = one signrot_swiglu_rotate_quant_int4 call
+    (reads gate and up, writes codes).  Beside it, the unfused pair it
+    replaces: the producer as a library elementwise kernel (torch, binary32
+    SiLU(gate) * up stored as bf16) and then signrot_rotate_quant_int4_outlier
+    on that x."""
+    gate_b, up_b, _ = W.swiglu_batch("n14336_t8192")
+    t, n = gate_b.shape
+    cg, cu, _ = W.swiglu_batch("n14336_t8192", tokens=256, stream=11)
+    stream = torch.cuda.current_stream()
+    g0, u0 = to_dev_bits(gate_b, torch), to_dev_bits(up_b, torch)
+    del gate_b, up_b
+    xcal = (torch.nn.functional.silu(to_dev_bits(cg, torch).float()) * to_dev_bits(cu, torch).float()).bfloat16()
+    _, c, _, mc = R.calibrate(xcal)
+    sigma = -1 if mc < 0 else 1
+    nsets = max(2, int(np.ceil(BUFFER_SETS_MIN_BYTES / (4 * t * n))))
+    gs = [g0] + [g0.clone() for _ in range(nsets - 1)]
+    us = [u0] + [u0.clone() for _ in range(nsets - 1)]
+    xs = [torch.empty((t, n), dtype=torch.bfloat16, device="cuda") for _ in range(nsets)]
+    outs = [(torch.empty((t, n // 2), dtype=torch.uint8, device="cuda"), torch.empty(t, device="cuda"),
+             torch.empty(t, device="cuda")) for _ in range(nsets)]
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    L = R.lib()
+
+    def fused(i):
+        k = i % nsets
+        st = L.signrot_swiglu_rotate_quant_int4(gs[k].data_ptr(), us[k].data_ptr(), t, n, n, c, sigma,
+                                                outs[k][0].data_ptr(), outs[k][1].data_ptr(),
+                                                outs[k][2].data_ptr(), None, sptr)
+        if st != 0:
+            R.check(st, "signrot_swiglu_rotate_quant_int4")
+
+    def producer_into(i):
+        k = i % nsets
+        xs[k].copy_(torch.nn.functional.silu(gs[k].float()).mul_(us[k].float()))
+
+    def rotate(i):
+        k = i % nsets
+        st = L.signrot_rotate_quant_int4_outlier(xs[k].data_ptr(), t, n, n, c, sigma, outs[k][0].data_ptr(),
+                                                 outs[k][1].data_ptr(), outs[k][2].data_ptr(), None, sptr)
+        if st != 0:
+            R.check(st, "signrot_rotate_quant_int4_outlier")
+
+    for i in range(nsets):
+        producer_into(i)
+    unf_rot = leg(torch, stream, rotate, 100, 200)
+    unf_prod = leg(torch, stream, producer_into, 20, 50)
+    for i in range(args.warmup):
+        fused(i)
+    head = timed_launches(torch, stream, fused, args.steps)
+    ms = head["mean_ms"]
+    fused_bytes = t * (4 * n + n // 2 + 8)  # gate + up in, codes + scale + zero out
+    achieved = fused_bytes / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "tokens/s and achieved HBM GB/s, SignRot rotate+INT4 with the SwiGLU producer fused in",
+        "value": t * args.steps / head["wall_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["wall_s"] * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"gate, up bf16 [{t} x {n}] (gate N(0,1.5), up N(0,0.6); massive channel {c} "
+                               "in 20% of tokens), x = bf16(SiLU(gate) * up) in the kernel",
+                   "kernel": R.kernel_name(n) + " (SwiGLU instance)",
+                   "launch_ms": {k: head[k] for k in ("mean_ms", "p10_ms", "p50_ms", "p90_ms", "group")},
+                   "unfused_producer_ms": unf_prod["mean_ms"],
+                   "unfused_rotate_ms": unf_rot["mean_ms"],
+                   "unfused_total_ms": unf_prod["mean_ms"] + unf_rot["mean_ms"],
+                   "hbm_bytes_fused": fused_bytes,
+                   "hbm_bytes_unfused": t * (4 * n + 2 * n) + t * (2 * n + n // 2 + 8)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "bytes_per_token": 4 * n + n // 2 + 8,
+                     "kernel_avg_ms": ms},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def cpu_baseline_linear(codes, scale, zero, wf, budget_s: float = 12.0) -> dict:
     """The oracle's int4_linear (float64 dequantize, then numpy matmul) on
     32-token chunks of the same operands, for about budget_s seconds."""
@@ -468,6 +547,9 @@ def main() -> int:
     ap.add_argument("--linear", action="store_true",
                     help="time the INT4-activation down-projection signrot_int4_linear instead "
                          "(8192 x 14336 codes, W' 4096 x 14336 bf16)")
+    ap.add_argument("--swiglu", action="store_true",
+                    help="time the online path with the SwiGLU producer fused in (gate, up 8192 x 14336 bf16) "
+                         "against the unfused producer + rotate pair")
     ap.add_argument("--workload", default=WORKLOAD,
                     choices=["n4096_t64", "n8192_t2048", "n14336_t4096", "n14336_t8192", "n28672_t8192",
                              "n11008_t8192"],
@@ -492,6 +574,8 @@ def main() -> int:
         return bench_fold(args, torch, R, W)
     if args.linear:
         return bench_linear(args, torch, R, W)
+    if args.swiglu:
+        return bench_swiglu(args, torch, R, W)
     L = R.lib()
 
     wname = args.workload

@@ -201,6 +201,35 @@ int signrot_rotate_quant_int4_zint(const void* x_bf16, int64_t tokens, int64_t n
                                    uint8_t* codes, float* scale, float* zero, void* stream);
 
 /*
+ * The online path with its producer fused in (explainer, paragraph on the
+ * down-projection: the gated nonlinearity between the up/gate projections and
+ * the down-projection is why the rotation has to run online).  The
+ * down-projection input is computed from the producer's two operands,
+ *   x = bf16(SiLU(gate) * up),  SiLU(z) = z / (1 + e^-z),
+ * in binary32 and rounded once to bf16 (nearest, ties to even), and then goes
+ * through exactly what signrot_rotate_quant_int4_outlier computes for that x;
+ * x itself never reaches memory.  (SwiGLU as the gated unit is a reading: the
+ * pages name the nonlinearity, not its formula.)  The binary32 SiLU is within
+ * about 2e-6 relative of the exact value for |gate| <= 16, so x equals the
+ * exactly rounded bf16 value except where that value lies that close to a
+ * point halfway between two bf16 numbers.
+ *
+ *   gate_bf16, up_bf16  device, [tokens][ld] bf16 each, same ld, 16-byte
+ *                       aligned; ld >= n, ld % 8 == 0.
+ *   c, sigma            the calibrated sign vector, as for
+ *                       signrot_rotate_quant_int4_outlier (calibrated on x).
+ *   codes, scale, zero, y_out   as for signrot_rotate_quant_int4.
+ *
+ * Only the widths with a fast kernel: n = 3584, 7168, 14336, 28672, 4096,
+ * 8192, 16384; any other supported n -> SIGNROT_EUNSUPPORTED_N.  Other errors
+ * as for signrot_rotate_quant_int4_outlier (a null or misaligned up ->
+ * SIGNROT_EINVAL).  No allocation.  Asynchronous.
+ */
+int signrot_swiglu_rotate_quant_int4(const void* gate_bf16, const void* up_bf16, int64_t tokens, int64_t n, int64_t ld,
+                                     int64_t c, int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
+                                     void* stream);
+
+/*
  * Dequantization (explainer, paragraph on the 4-bit quantizer: a token's 16
  * levels are spread evenly from its smallest to its largest value, so code q
  * stands for the level mn + q * scale; paragraph on symmetric versus

@@ -92,7 +92,7 @@ def bf16_midpoint_distance(x: np.ndarray) -> np.ndarray:
     margin by which a rounding to bf16 is decided."""
     x = np.asarray(x, dtype=np.float64)
     f, e = np.frexp(x)
-    g = np.abs(f) * 256.0  # significand in [128, 256)
+    g = np.where(x == 0, 256.0, np.abs(f) * 256.0)  # significand in [128, 256)
     d = np.abs(g - np.floor(g) - 0.5) / g
     return np.where(x == 0, np.inf, d)
 

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.signrot_rotate_quant_int4.restype = ctypes.c_int
     L.signrot_rotate_quant_int4_outlier.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
     L.signrot_rotate_quant_int4_outlier.restype = ctypes.c_int
+    L.signrot_swiglu_rotate_quant_int4.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp, vp]
+    L.signrot_swiglu_rotate_quant_int4.restype = ctypes.c_int
     L.signrot_rotate_quant_int4_zint.argtypes = [vp, i64, i64, i64, i64, ctypes.c_int, vp, vp, vp, vp]
     L.signrot_rotate_quant_int4_zint.restype = ctypes.c_int
     L.signrot_dequant.argtypes = [vp, vp, vp, i64, i64, vp, vp]
@@ -92,6 +94,7 @@ EXPORTED = (
     "signrot_rotate_quant_int4",
     "signrot_rotate_quant_int4_outlier",
     "signrot_rotate_quant_int4_zint",
+    "signrot_swiglu_rotate_quant_int4",
     "signrot_dequant",
     "signrot_fold_weights",
     "signrot_weight_rowsum",
@@ -268,6 +271,30 @@ def signrot_rotate_quant_int4_zint(x, c: int, sigma: int, out=None):
     return codes, scale, zero
 
 
+def signrot_swiglu_rotate_quant_int4(gate, up, c: int, sigma: int, y_out: bool = False, out=None):
+    """The online path on x = bf16(SiLU(gate) * up), the producer fused in:
+    gate and up bf16 [T, n] (same row stride) -> (codes, scale, zero[, y])."""
+    import torch
+
+    ptr, t, n, ld = _rows(gate)
+    uptr, tu, nu, ldu = _rows(up)
+    if (tu, nu) != (t, n) or (t > 1 and ldu != ld):
+        raise ValueError("gate and up must have the same shape and row stride")
+    if out is None:
+        codes = torch.empty((t, n // 2), dtype=torch.uint8, device=gate.device)
+        scale = torch.empty(t, dtype=torch.float32, device=gate.device)
+        zero = torch.empty(t, dtype=torch.float32, device=gate.device)
+        y = torch.empty((t, n), dtype=torch.float32, device=gate.device) if y_out else None
+    else:
+        codes, scale, zero = out[:3]
+        y = out[3] if len(out) > 3 else None
+    check(lib().signrot_swiglu_rotate_quant_int4(ptr, uptr, t, n, ld, int(c), int(sigma), codes.data_ptr(),
+                                                 scale.data_ptr(), zero.data_ptr(),
+                                                 y.data_ptr() if y is not None else None, _stream_of(gate)),
+          "signrot_swiglu_rotate_quant_int4")
+    return (codes, scale, zero, y) if y is not None else (codes, scale, zero)
+
+
 def signrot_dequant(codes, scale, zero, n: int | None = None):
     """codes u8 [T, n/2], scale/zero f32 [T] -> y_hat f32 [T, n]."""
     import torch
@@ -361,6 +388,7 @@ calibrate = signrot_calibrate
 rotate_quant_int4 = signrot_rotate_quant_int4
 rotate_quant_int4_outlier = signrot_rotate_quant_int4_outlier
 rotate_quant_int4_zint = signrot_rotate_quant_int4_zint
+swiglu_rotate_quant_int4 = signrot_swiglu_rotate_quant_int4
 dequant = signrot_dequant
 fold_weights = signrot_fold_weights
 weight_rowsum = signrot_weight_rowsum

@@ -388,11 +388,17 @@ int signrot_rotate_quant_int4(const void* x_bf16, int64_t tokens, int64_t n, int
 
 namespace {
 int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c, int sigma,
-                              uint8_t* codes, float* scale, float* zero, float* y_out, int zint, void* stream) {
+                              uint8_t* codes, float* scale, float* zero, float* y_out, int zint, void* stream,
+                              const void* up_bf16 = nullptr) {
   g_last_error[0] = '\0';
   const Shape sh = factor_n(n);
   if (!sh.ok) {
     set_error("unsupported n=%s", std::to_string(n).c_str());
+    return SIGNROT_EUNSUPPORTED_N;
+  }
+  if (up_bf16 && rq_kernel_for(sh) != RqKernel::kFast) {
+    set_error("n=%s: the fused SwiGLU producer runs on the fast widths only (3584, 7168, 14336, 28672, 4096, 8192, "
+              "16384)", std::to_string(n).c_str());
     return SIGNROT_EUNSUPPORTED_N;
   }
   if (c < 0 || c >= n) return fail_einval("c must be a channel in [0, n)");
@@ -406,9 +412,11 @@ int rotate_quant_outlier_impl(const void* x_bf16, int64_t tokens, int64_t n, int
   if (!aligned16(x_bf16)) return fail_einval("x must be 16-byte aligned");
   if (!aligned16(codes)) return fail_einval("codes must be 16-byte aligned");
   if (y_out && !aligned16(y_out)) return fail_einval("y_out must be 16-byte aligned");
+  if (up_bf16 && !aligned16(up_bf16)) return fail_einval("up must be 16-byte aligned");
   RqArgs a;
   memset(&a, 0, sizeof(a));
   a.x = static_cast<const uint16_t*>(x_bf16);
+  a.x2 = static_cast<const uint16_t*>(up_bf16);
   a.codes = codes;
   a.scale = scale;
   a.zero = zero;
@@ -463,6 +471,17 @@ int signrot_rotate_quant_int4_outlier(const void* x_bf16, int64_t tokens, int64_
 int signrot_rotate_quant_int4_zint(const void* x_bf16, int64_t tokens, int64_t n, int64_t ld, int64_t c, int sigma,
                                    uint8_t* codes, float* scale, float* zero, void* stream) {
   return rotate_quant_outlier_impl(x_bf16, tokens, n, ld, c, sigma, codes, scale, zero, nullptr, 1, stream);
+}
+
+int signrot_swiglu_rotate_quant_int4(const void* gate_bf16, const void* up_bf16, int64_t tokens, int64_t n, int64_t ld,
+                                     int64_t c, int sigma, uint8_t* codes, float* scale, float* zero, float* y_out,
+                                     void* stream) {
+  if (tokens > 0 && !up_bf16) {
+    g_last_error[0] = '\0';
+    return fail_einval("null device pointer");
+  }
+  return rotate_quant_outlier_impl(gate_bf16, tokens, n, ld, c, sigma, codes, scale, zero, y_out, 0, stream,
+                                   tokens > 0 ? up_bf16 : nullptr);
 }
 
 int signrot_fold_weights(const void* w_bf16, int64_t rows, int64_t n, int64_t ld, const int8_t* d, float* w_out,

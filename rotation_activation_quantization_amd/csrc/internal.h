@@ -66,7 +66,8 @@ H28Masks h28_masks();
 // Everything a rotate+quant kernel needs, passed by value as the kernel
 // argument block.
 struct RqArgs {
-  const uint16_t* x;   // bf16 bits, [tokens][ld]
+  const uint16_t* x;   // bf16 bits, [tokens][ld] (SwiGLU entry point: the gate)
+  const uint16_t* x2;  // SwiGLU entry point: up, bf16 bits [tokens][ld] (x = bf16(SiLU(gate) * up)); else null
   const int8_t* d;     // [n], +-1
   uint8_t* codes;      // [tokens][n/2]
   float* scale;        // [tokens]

@@ -88,7 +88,27 @@ __device__ __forceinline__ uint32_t quad_slot(uint32_t q) {
 // MAYBE_GENERAL: d arrived as a vector and may lack the calibrated form; the
 // body then takes `general` (a wave-uniform flag) at run time, so that both
 // cases share one register allocation.  Without it d is given as (c, sigma).
-template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false>
+// x = bf16(SiLU(gate) * up) for the eight bf16 pairs of two 16-byte chunks:
+// SiLU(z) = z / (1 + e^-z) with e^-z = 2^(-z log2 e) (v_exp_f32) and the
+// reciprocal v_rcp_f32, in binary32, rounded once to bf16 by the hardware
+// conversion (nearest, ties to even).  Relative error before that rounding
+// stays below about 2e-6 for |gate| <= 16.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+__device__ __forceinline__ u32x4_t swiglu_chunk(const u32x4_t& g, const u32x4_t& u) {
+  u32x4_t x;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = silu_f32(bf16_lo(g[k])) * bf16_lo(u[k]);
+    const float hi = silu_f32(bf16_hi(g[k])) * bf16_hi(u[k]);
+    x[k] = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(lo), static_cast<__bf16>(hi)});
+  }
+  return x;
+}
+
+template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false, bool SWIGLU = false>
 __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbits, const uint32_t* h28,
                              const DForm& form, float* red, float* xcl) {
   using S = FastShape<KA, KB>;
@@ -148,6 +168,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     }
   };
   u32x4_t st[S::CPT];
+  u32x4_t stu[SWIGLU ? S::CPT : 1];  // SwiGLU: the up chunks beside the gate chunks in st
   // Row loads through a buffer resource on the row (scalar base, the
   // wave-uniform unit offset as the scalar offset, the lane offset gl), so no
   // per-lane 64-bit address is kept across the loop.
@@ -156,6 +177,12 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 #pragma unroll
     for (int i = 0; i < S::CPT; ++i)
       st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, gl, unit_g(i), kNontemporal));
+    if constexpr (SWIGLU) {
+      const __amdgpu_buffer_rsrc_t ru = buffer_rsrc(a.x2 + r * a.ld, 2u * S::N);
+#pragma unroll
+      for (int i = 0; i < S::CPT; ++i)
+        stu[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, gl, unit_g(i), kNontemporal));
+    }
   };
   // The first row's loads go out before the weights are built (all but the
   // 56-row shape, whose registers are short), so their latency overlaps the
@@ -227,6 +254,10 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int64_t grid = gridDim.x;
 
   auto write_row = [&](uint32_t bo, int xslot) {
+    if constexpr (SWIGLU) {
+#pragma unroll
+      for (int i = 0; i < S::CPT; ++i) st[i] = swiglu_chunk(st[i], stu[i]);
+    }
     if (xc_thread) {
 #pragma unroll
       for (int i = 0; i < S::CPT; ++i) {
@@ -437,7 +468,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
 }
 
 // DVEC: d is a vector (its form is decided here); otherwise (c, sigma) given.
-template <int KA, int KB, bool DVEC, bool YOUT, bool ZINT = false>
+template <int KA, int KB, bool DVEC, bool YOUT, bool ZINT = false, bool SWIGLU = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
 void rq_fast_kernel(RqArgs a) {
   using S = FastShape<KA, KB>;
@@ -467,7 +498,7 @@ void rq_fast_kernel(RqArgs a) {
     __syncthreads();
     form = decode_d_form_fast(a, dbits, h28_lds, scratch);
   }
-  rq_fast_body<KA, KB, DVEC, YOUT, ZINT>(a, lds, dbits, h28_lds, form, red, xcl);
+  rq_fast_body<KA, KB, DVEC, YOUT, ZINT, SWIGLU>(a, lds, dbits, h28_lds, form, red, xcl);
 }
 
 template <int KA, int KB>
@@ -490,7 +521,10 @@ hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
   if (grid > a.tokens) grid = a.tokens;
   const dim3 blocks(static_cast<unsigned>(grid));
   const dim3 threads(static_cast<unsigned>(S::kThreads));
-  if (a.zint)  // only with d given as (c, sigma), and no y_out
+  if (a.x2)  // SwiGLU producer fused in: d given as (c, sigma)
+    (a.yout ? rq_fast_kernel<KA, KB, false, true, false, true> : rq_fast_kernel<KA, KB, false, false, false, true>)
+        <<<blocks, threads, 0, stream>>>(a);
+  else if (a.zint)  // only with d given as (c, sigma), and no y_out
     rq_fast_kernel<KA, KB, false, false, true><<<blocks, threads, 0, stream>>>(a);
   else if (a.form_given)
     (a.yout ? rq_fast_kernel<KA, KB, false, true> : rq_fast_kernel<KA, KB, false, false>)<<<blocks, threads, 0, stream>>>(a);

@@ -182,3 +182,16 @@ def swiglu_batch(name: str, tokens: int | None = None, stream: int = 10):
         gate[r0:r1] = f32_to_bf16_bits(gv)
         up[r0:r1] = f32_to_bf16_bits(uv)
     return gate, up, {"channel": c, "outlier_tokens": np.flatnonzero(has)}
+
+
+def swiglu_rows(tokens: int, n: int, seed: int, outlier: float = 1500.0):
+    """Small generic gate / up rows (bf16 bits [T, n] each) for edge-case tests:
+    gate ~ N(0, 1.5), up ~ N(0, 0.6); channel (seed % n) gets gate = 8 and
+    up = outlier / 8 in every third token."""
+    g = np.random.default_rng([SEED_ROOT, 98, seed])
+    gv = g.standard_normal((tokens, n), dtype=np.float32) * np.float32(1.5)
+    uv = g.standard_normal((tokens, n), dtype=np.float32) * np.float32(0.6)
+    if outlier and n:
+        gv[::3, seed % n] = np.float32(8.0)
+        uv[::3, seed % n] = np.float32(outlier / 8.0)
+    return f32_to_bf16_bits(gv), f32_to_bf16_bits(uv)

@@ -143,6 +143,23 @@ def test_calibrate_noalloc_argument_errors(L):
     assert cal(x=FAKE + 2) == R.SIGNROT_EINVAL
 
 
+def test_swiglu_rotate_quant_argument_errors(L):
+    def sw(g=FAKE, u=FAKE, t=4, n=14336, ld=14336, c=3, sig=1, co=FAKE, s=FAKE, z=FAKE):
+        return L.signrot_swiglu_rotate_quant_int4(g, u, t, n, ld, c, sig, co, s, z, None, None)
+
+    assert sw(n=11008, ld=11008) == R.SIGNROT_EUNSUPPORTED_N  # no fast kernel at this width
+    assert b"fast widths" in L.signrot_last_error()
+    assert sw(n=6) == R.SIGNROT_EUNSUPPORTED_N
+    assert sw(u=None) == R.SIGNROT_EINVAL
+    assert sw(u=FAKE + 8) == R.SIGNROT_EINVAL
+    assert sw(g=None) == R.SIGNROT_EINVAL
+    assert sw(c=14336) == R.SIGNROT_EINVAL
+    assert sw(sig=0) == R.SIGNROT_EINVAL
+    assert sw(ld=100) == R.SIGNROT_EINVAL
+    assert sw(t=-1) == R.SIGNROT_EINVAL
+    assert sw(t=0, g=None, u=None, co=None, s=None, z=None) == R.SIGNROT_OK
+
+
 def test_dequant_argument_errors(L):
     def dq(c=FAKE, s=FAKE, z=FAKE, t=3, n=4096, y=FAKE):
         return L.signrot_dequant(c, s, z, t, n, y, None)
