@@ -52,7 +52,10 @@ BUFFER_SETS_MIN_BYTES = 1.2 * 2**30
 # rocprofv3 counters is reported only while they are unchanged.
 # (plus the compile flags, build.COMMON)
 _CSRC = "rotation_activation_quantization_amd/csrc/"
-KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "wave_ops.h", _CSRC + "device_common.h", _CSRC + "internal.h")
+KERNEL_SOURCES = (_CSRC + "rq_fast.hip", _CSRC + "rq_fast_common.h", _CSRC + "wave_ops.h", _CSRC + "device_common.h",
+                  _CSRC + "internal.h")
+HALVES_SOURCES = (_CSRC + "rq_halves.hip", _CSRC + "rq_fast_common.h", _CSRC + "wave_ops.h", _CSRC + "device_common.h",
+                  _CSRC + "internal.h")
 GENERIC_SOURCES = (_CSRC + "rq_generic.hip", _CSRC + "device_common.h", _CSRC + "internal.h")
 OUTER_SOURCES = (_CSRC + "rq_outer_impl.h", _CSRC + "rq_outer.hip", _CSRC + "rq_outer_t1.hip", _CSRC + "rq_outer_t2.hip",
                  _CSRC + "rq_outer_t4.hip", _CSRC + "rq_outer_t8.hip", _CSRC + "rq_outer_t16.hip", _CSRC + "wave_ops.h",
@@ -61,7 +64,8 @@ TRAFFIC_PROFILE = "profiles/{kernel}_n{n}_t{t}_hbm_traffic.txt"
 
 
 def kernel_sources(kernel: str):
-    return {"rq_generic": GENERIC_SOURCES, "rq_outer_mfma": OUTER_SOURCES}.get(kernel, KERNEL_SOURCES)
+    return {"rq_generic": GENERIC_SOURCES, "rq_outer_mfma": OUTER_SOURCES,
+            "rq_mfma28x2_w7": HALVES_SOURCES}.get(kernel, KERNEL_SOURCES)
 
 
 def kernel_source_digest(kernel: str = "") -> str:

@@ -370,7 +370,7 @@ int signrot_outer_fold(int64_t n);
  * static string naming it), or NULL when n is unsupported:
  *   "rq_mfma32_w8"   n = 4096, 8192, 16384 (Sylvester);
  *   "rq_mfma28_w7"   n = 28 * 2^k, k = 7, 8, 9;
- *   "rq_mfma56_w14"  n = 28672;
+ *   "rq_mfma28x2_w7" n = 28672 (two halves of the 14336 transform);
  *   "rq_outer_mfma"  n = m * 2^k with 16 <= 2^k <= 256 and ceil(m / 32)
  *                    at most 12, 12, 8, 6, 4 for 2^k = 16, 32, 64, 128, 256
  *                    (11008, 13824, 18944, 8960, 27648, 5120, 5504, 896,

@@ -19,6 +19,7 @@ SOURCES = [
     "api.hip",
     "rq_generic.hip",
     "rq_fast.hip",
+    "rq_halves.hip",
     "rq_outer.hip",
     "rq_outer_t1.hip",
     "rq_outer_t2.hip",

@@ -1,13 +1,13 @@
 // Fused rotate + sign flip + per-token asymmetric INT4 for gfx950: the fast
 // kernels for n = 28 * 2^k, k = 7..9 (3584, 7168, 14336 -- the LLaMA3-8B
-// down-projection input; seven waves per token row), n = 56 * 2^9 (28672, the
-// LLaMA3-70B one; fourteen waves) and n = 2^12, 2^13, 2^14 (eight waves).
+// down-projection input; seven waves per token row) and n = 2^12, 2^13, 2^14
+// (eight waves).  n = 28 * 2^10 (28672, the LLaMA3-70B one) runs as two halves
+// of the n = 14336 transform (rq_halves.hip).
 //
 // Index split.  A row x[i], i = a * 2^KB + b (a < KA, b < 2^KB), is read as
 // quads: b = 4 q + bb (q < NQ = 2^(KB-2), bb < 4).  The transform
-// H = H_KA (x) H_{2^KB} (KA = 28: Paley's order-28 matrix; KA = 56: H28 (x) H2,
-// so that H28 (x) H_1024 reads as H56 (x) H_512 with a = 2 a28 + (top bit of
-// b); KA = 32: the Sylvester matrix, so H is the Sylvester matrix of order n)
+// H = H_KA (x) H_{2^KB} (KA = 28: Paley's order-28 matrix; KA = 32: the
+// Sylvester matrix, so H is the Sylvester matrix of order n)
 // -- explainer
 // "SignRot for 4-bit LLM quantization", paragraphs on rotation and on the
 // down-projection: a Hadamard matrix applied as a fast Walsh-Hadamard
@@ -46,68 +46,14 @@
 
 #include <atomic>
 
-#include "device_common.h"
-#include "wave_ops.h"
+#include "rq_fast_common.h"
 
 namespace signrot {
 namespace {
 
-using namespace wave;
-
-template <int KA, int KB>
-struct FastShape {
-  static_assert(KA == 28 || KA == 32 || KA == 56, "order-28, order-56 or Sylvester outer factor");
-  static_assert(KB >= 7 && KB <= 9, "2 to 8 register tiles");
-  static constexpr int kWaves = KA / 4;
-  static constexpr int NKC = (KA + 7) / 8;       // K chunks of eight a-rows
-  static constexpr int kThreads = 64 * kWaves;
-  static constexpr int NQ = 1 << (KB - 2);       // quads per a-row
-  static constexpr int NT = NQ / 16;             // register tiles
-  static constexpr int LG = (NT == 8) ? 3 : (NT == 4) ? 2 : 1;
-  static constexpr int NV = 4 * NT;              // values per lane
-  static constexpr int PB = 16 * NQ;             // bytes per pair-row
-  static constexpr int kRowBytes = (KA / 2) * PB;
-  // KA = 28: the fourth K chunk reads "pairs" 14 and 15 for lanes whose
-  // weights are zero; two zero pair-rows behind the second buffer keep those
-  // reads finite (for the first buffer they land in the second).
-  static constexpr int kLdsBytes = 2 * kRowBytes + (KA == 28 ? 2 * PB : 0);
-  static constexpr int CR = NQ / 2;              // 16-byte chunks per a-row
-  static constexpr int CPT = CR / 16;            // chunks per thread per row
-  static constexpr uint32_t KMUL = 256u + 128u / NT;
-  static constexpr uint32_t SWZ = 8u / NT;
-  static constexpr int N = KA << KB;
-};
-
-template <int KA, int KB>
-__device__ __forceinline__ uint32_t quad_slot(uint32_t q) {
-  using S = FastShape<KA, KB>;
-  const uint32_t u = q & (S::NT - 1);
-  return 16u * u + ((q >> S::LG) ^ (u * S::SWZ));
-}
-
 // MAYBE_GENERAL: d arrived as a vector and may lack the calibrated form; the
 // body then takes `general` (a wave-uniform flag) at run time, so that both
 // cases share one register allocation.  Without it d is given as (c, sigma).
-// x = bf16(SiLU(gate) * up) for the eight bf16 pairs of two 16-byte chunks:
-// SiLU(z) = z / (1 + e^-z) with e^-z = 2^(-z log2 e) (v_exp_f32) and the
-// reciprocal v_rcp_f32, in binary32, rounded once to bf16 by the hardware
-// conversion (nearest, ties to even).  Relative error before that rounding
-// stays below about 2e-6 for |gate| <= 16.
-__device__ __forceinline__ float silu_f32(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
-}
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-__device__ __forceinline__ u32x4_t swiglu_chunk(const u32x4_t& g, const u32x4_t& u) {
-  u32x4_t x;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float lo = silu_f32(bf16_lo(g[k])) * bf16_lo(u[k]);
-    const float hi = silu_f32(bf16_hi(g[k])) * bf16_hi(u[k]);
-    x[k] = __builtin_bit_cast(uint32_t, bf16x2_t{static_cast<__bf16>(lo), static_cast<__bf16>(hi)});
-  }
-  return x;
-}
-
 template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false, bool SWIGLU = false>
 __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbits, const uint32_t* h28,
                              const DForm& form, float* red, float* xcl) {
@@ -115,7 +61,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const bool general = MAYBE_GENERAL && __builtin_amdgcn_readfirstlane(form.structured) == 0;
   constexpr int NT = S::NT;
   constexpr int NV = S::NV;
-  constexpr bool kLateStage = (KA == 56);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,11 +129,9 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
         stu[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, gl, unit_g(i), kNontemporal));
     }
   };
-  // The first row's loads go out before the weights are built (all but the
-  // 56-row shape, whose registers are short), so their latency overlaps the
-  // set-up; that matters most for a few tokens per call.
-  constexpr bool kEarlyLoad = (KA != 56);
-  if (kEarlyLoad && static_cast<int64_t>(blockIdx.x) < a.tokens) load_row(blockIdx.x);
+  // The first row's loads go out before the weights are built, so their
+  // latency overlaps the set-up; that matters most for a few tokens per call.
+  if (static_cast<int64_t>(blockIdx.x) < a.tokens) load_row(blockIdx.x);
 
   // MFMA weights, A operand: lane (g, nl) holds A[m = nl][k = 8 g + i] with
   // m -> (a' = 4 w + (nl >> 2), c = nl & 3), k -> (a = 8 kc + 2 g + (i >> 2), bb = i & 3).
@@ -286,7 +229,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   int64_t nxt = cur + grid;
   int64_t nn = nxt + grid;
   if (cur >= tokens) return;
-  if (!kEarlyLoad) load_row(cur);
   wait_vmcnt<0>();
   write_row(0u, 0);
   if (nxt < tokens) load_row(nxt);
@@ -297,16 +239,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     const int par = it & 1;
     const uint32_t bo = par ? static_cast<uint32_t>(S::kRowBytes) : 0u;
 
-    // (0) KA = 56 stages the next row here, before the MFMA stage, so that
-    // its registers are not live while the operands and the 28 weight
-    // registers are (the other shapes do it in (2), a longer lead time).
-    if (kLateStage && nxt < tokens) {
-      if (it == 0) wait_vmcnt<0>();
-      else if (YOUT) wait_vmcnt<1 + NT>();
-      else wait_vmcnt<1>();
-      write_row(bo ^ static_cast<uint32_t>(S::kRowBytes), par ^ 1);
-    }
-
     // (1) MFMA stage from this row's buffer
     float v[NV];
     {
@@ -315,31 +247,19 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       for (int t = 0; t < NT; ++t) {
         const uint8_t* tp = lds + (base ^ (S::KMUL * t));
         f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        // operands in groups of four chunks, or two for the seven chunks of
-        // KA = 56 (whose 28 weight registers leave less room)
-        constexpr int kGroup = S::NKC > 4 ? 2 : 4;
+        u32x4_t b[S::NKC];
 #pragma unroll
-        for (int k0 = 0; k0 < S::NKC; k0 += kGroup) {
-          u32x4_t b[kGroup];
+        for (int kc = 0; kc < S::NKC; ++kc) b[kc] = *reinterpret_cast<const u32x4_t*>(tp + 4 * S::PB * kc);
 #pragma unroll
-          for (int kc = 0; kc < kGroup; ++kc)
-            if (k0 + kc < S::NKC) b[kc] = *reinterpret_cast<const u32x4_t*>(tp + 4 * S::PB * (k0 + kc));
-#pragma unroll
-          for (int kc = 0; kc < kGroup; ++kc)
-            if (k0 + kc < S::NKC)
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[k0 + kc], __builtin_bit_cast(bf16x8_t, b[kc]), acc, 0,
-                                                            0, 0);
-          if (S::NKC > 4) __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int kc = 0; kc < S::NKC; ++kc)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[kc], __builtin_bit_cast(bf16x8_t, b[kc]), acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[4 * t + r] = acc[r];
       }
     }
 
     // (2) stage the next row into the other buffer; start loading the one after
-    if (kLateStage) {
-      if (nn < tokens) load_row(nn);
-    } else if (nxt < tokens) {
+    if (nxt < tokens) {
       // The loads were issued a row ago; after them every wave issued the
       // previous row's code store (plus NT y stores with y_out); wave 0 also
       // scale and zero, so the same count only makes it wait longer.
@@ -442,7 +362,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     const __amdgpu_buffer_rsrc_t cs = buffer_rsrc(a.codes + row * static_cast<int64_t>(S::N / 2), S::N / 2);
     const uint32_t coff = static_cast<uint32_t>(chan0 / 2);
     if constexpr (NT == 8) {
-      __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0, kNontemporal);
+      store_b128_held<kNontemporal>(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0);
     } else if constexpr (NT == 4) {
       __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{q[0], q[1]}, cs, coff, 0, kNontemporal);
     } else {
@@ -455,7 +375,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
         f32x4_t o;
 #pragma unroll
         for (int k = 0; k < 4; ++k) o[k] = (v[4 * e4 + k] + shift) * a.inv_sqrt_n;
-        *reinterpret_cast<f32x4_t*>(yp + 4 * e4) = o;
+        store_f32x4_held(yp + 4 * e4, o);
       }
     }
 
@@ -546,7 +466,7 @@ hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s) {
       case 7: return launch_shape<28, 7>(a, s);
       case 8: return launch_shape<28, 8>(a, s);
       case 9: return launch_shape<28, 9>(a, s);
-      default: return launch_shape<56, 9>(a, s);  // 28 * 2^10 read as 56 * 2^9
+      default: return launch_rq_halves(a, s);  // 28 * 2^10 as two halves of 28 * 2^9
     }
   }
   if (a.n == 4096) return launch_shape<32, 7>(a, s);
@@ -555,7 +475,7 @@ hipError_t launch_rq_fast(const RqArgs& a, hipStream_t s) {
 }
 
 const char* rq_fast_name(int n) {
-  if (n == 28672) return "rq_mfma56_w14";
+  if (n == 28672) return "rq_mfma28x2_w7";
   if (n % 28 == 0) return "rq_mfma28_w7";
   return "rq_mfma32_w8";
 }

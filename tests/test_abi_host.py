@@ -277,7 +277,7 @@ def test_rotate_kernel_choice():
     for n in (2, 28, 56, 1792, 3584, 7168, 14336, 28672, 2048, 4096, 8192, 16384, 32768):
         name = R.kernel_name(n)
         if n == 28672:
-            assert name == "rq_mfma56_w14"
+            assert name == "rq_mfma28x2_w7"
         elif n in fast28:
             assert name == "rq_mfma28_w7"
         elif n in (4096, 8192, 16384):
@@ -338,7 +338,7 @@ def _expected_kernel(n):
     if m == 28 and k in (7, 8, 9):
         return "rq_mfma28_w7"
     if n == 28672:
-        return "rq_mfma56_w14"
+        return "rq_mfma28x2_w7"
     def outer_ok(mm, kk):
         if mm <= 1 or mm % 4 or mm > 512 or not 4 <= kk <= 8:
             return False
@@ -370,7 +370,7 @@ def test_kernel_dispatch_rule():
         want = _expected_kernel(n)
         assert R.kernel_name(n) == want, (n, R.kernel_name(n), want)
         seen.add(want)
-    assert seen == {"rq_mfma32_w8", "rq_mfma28_w7", "rq_mfma56_w14", "rq_outer_mfma", "rq_generic"}
+    assert seen == {"rq_mfma32_w8", "rq_mfma28_w7", "rq_mfma28x2_w7", "rq_outer_mfma", "rq_generic"}
 
 
 @pytest.mark.parametrize("m,fold", [(1, 2), (1, 4), (1, 7), (12, 3), (20, 3), (12, 5), (28, 1), (28, 4), (108, 2),
