@@ -71,6 +71,44 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def resource_report(sources=None) -> dict:
+    """Compile sources (all .hip by default) with the compiler's
+    kernel-resource-usage remarks and return {mangled kernel name:
+    {"vgprs", "agprs", "scratch", "occupancy"}} (scratch in bytes per lane;
+    nonzero means the kernel spills registers)."""
+    import re
+    import tempfile
+
+    srcs = sources or [s for s in SOURCES if s.endswith(".hip")]
+    keys = {"VGPRs": "vgprs", "AGPRs": "agprs", "ScratchSize [bytes/lane]": "scratch",
+            "Occupancy [waves/SIMD]": "occupancy"}
+
+    def one(src):
+        with tempfile.TemporaryDirectory() as td:
+            cmd = [hipcc(), *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", os.path.join(td, "x.o"),
+                   "-Rpass-analysis=kernel-resource-usage"]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-2000:]}")
+        out, cur = {}, None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark:\s+(.+?): (\S+) \[-Rpass-analysis", line)
+            if not m:
+                continue
+            k, v = m.group(1).strip(), m.group(2)
+            if k == "Function Name":
+                cur = out.setdefault(v, {})
+            elif cur is not None and k in keys:
+                cur[keys[k]] = int(v)
+        return out
+
+    res = {}
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        for part in ex.map(one, srcs):
+            res.update(part)
+    return res
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libsignrot.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
@@ -88,4 +126,11 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--resources" in sys.argv:
+        # registers and spills per kernel instance, spilling ones first
+        rep = resource_report()
+        for name, r in sorted(rep.items(), key=lambda kv: (-kv[1].get("scratch", 0), kv[0])):
+            print(f"{r.get('vgprs', 0):4d} VGPR {r.get('agprs', 0):4d} AGPR {r.get('scratch', 0):4d} B/lane scratch "
+                  f"{r.get('occupancy', 0):2d} waves/SIMD  {name}")
+    else:
+        print(build(verbose="-v" in sys.argv))

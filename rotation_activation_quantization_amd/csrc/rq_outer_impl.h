@@ -483,10 +483,14 @@ hipError_t launch_outer_shape(const RqArgs& a, hipStream_t stream) {
 
 // The built shapes: (K chunks, column tiles, M-tiles per wave).  MTW keeps
 // the weights of a wave (4 MTW KC VGPRs for the whole launch), its
-// accumulators and its staging registers within the register share that its
-// launch bound (ceil(2 KC / MTW) waves per work-group) leaves, without
-// spills, and the work-group within 16 waves.  One translation unit per
-// column-tile count instantiates them.
+// accumulators and its staging registers near the register share that its
+// launch bound (ceil(2 KC / MTW) waves per work-group) leaves, and the
+// work-group within 16 waves.  The shapes with KC >= 9 and MTW = 2 reach 168
+// VGPRs and still spill 8-56 bytes per lane, as does KC = 4 with 16 column
+// tiles and y_out (python -m rotation_activation_quantization_amd.build
+// --resources lists every instance); separate instances for the two forms of
+// d remove those spills but ran slower at n = 11008.  One translation unit
+// per column-tile count instantiates them.
 #define SR_OUTER_SHAPES_T1(X)                                                                                   \
   X(1, 1, 2) X(2, 1, 2) X(3, 1, 2) X(4, 1, 2) X(5, 1, 2) X(6, 1, 2) X(7, 1, 2) X(8, 1, 2) X(9, 1, 2) X(10, 1, 2) \
   X(11, 1, 2) X(12, 1, 2)
