@@ -78,6 +78,14 @@ def test_swiglu_fused_matches_oracle(n):
     check(gate, up, f"n={n}")
 
 
+@pytest.mark.parametrize("n", [28672, 14336])
+def test_swiglu_fused_several_rows_per_work_group(n):
+    """600 tokens: more rows than resident work-groups, so that work-groups
+    take a second row while the first is processed."""
+    gate, up = W.swiglu_rows(600, n, seed=n + 7)
+    check(gate, up, f"n={n} T=600")
+
+
 @pytest.mark.timeout(600)
 def test_swiglu_fused_full_batch_n14336():
     """Every row of an 8192-token batch at n = 14336, calibrated on its own

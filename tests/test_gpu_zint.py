@@ -69,7 +69,7 @@ def compare_zint(y, codes, scale, zero, label):
 
 
 @pytest.mark.parametrize("n,t", [(4096, 64), (8192, 40), (14336, 48), (28672, 12), (3584, 40), (16384, 10),
-                                 (28, 9), (1792, 17)])
+                                 (28, 9), (1792, 17), (28672, 600)])
 def test_zint_matches_oracle(n, t):
     g = np.random.default_rng([83, n])
     for c, sigma in ((int(g.integers(n)), 1), (int(g.integers(n)), -1)):
