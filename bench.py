@@ -23,9 +23,14 @@ and the integer zero-point variant.  The line also reports per-launch
 percentiles, the quantization MSE of the GPU's own outputs, and the
 decode-sized latency.
 
+With the default workload the line also times the other configurations
+(n = 4096 x 64, 8192 x 2048, 14336 x 4096, 28672 x 8192 tokens) after the
+headline, each beside the traffic-ceiling kernel on the same buffers.
+
 Prints one JSON line.  Flags: --gpus N (only 1 is supported), --steps K,
 --warmup W, --workload W, --no-cpu-baseline, --no-decode (skip the
-decode-latency leg), --pmc-copy (also run plain copies of known size for the
+decode-latency leg and the other configurations, so that only the named
+workload's kernels run), --pmc-copy (also run plain copies of known size for the
 counter calibration of a rocprofv3 --pmc run); --fold times the offline weight
 fold, --linear the INT4-activation down-projection and --swiglu the path with
 the SwiGLU producer fused in, instead.
@@ -561,7 +566,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              "the path shards tokens across GPUs with no exchange, see the design notes.",
+              "tokens shard across GPUs with no exchange between them (each GPU rotates and quantizes its own rows).",
               file=sys.stderr)
         return 2
 
@@ -723,10 +728,64 @@ def main() -> int:
     if not args.no_decode and n == 14336:
         line["decode"] = {"workload": "n=14336, 1/4/16 tokens per call, same law; 10^4 calls",
                           "tokens": decode_latency(R, W, torch, c, sigma)}
+    if not args.no_decode and wname == WORKLOAD and args.tokens is None:
+        del xs, outs, calls, dcalls
+        torch.cuda.empty_cache()
+        line["other_configs"] = {name: config_leg(R, W, torch, L, name) for name in OTHER_CONFIGS}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy())
     print(json.dumps(line), flush=True)
     return 0
+
+
+OTHER_CONFIGS = ("n4096_t64", "n8192_t2048", "n14336_t4096", "n28672_t8192")
+
+
+def config_leg(R, W, torch, L, name: str, warmup: int = 100, steps: int = 200) -> dict:
+    """One more configuration on the (c, sigma) entry point: its own synthetic
+    batch and calibration, input copies rotated so that each launch reads
+    HBM (at most 64 copies: the 64-token batch stays cache-resident and is
+    launch-bound), the traffic-ceiling kernel on the same buffers first."""
+    bits, _ = W.batch(name)
+    t, n = bits.shape
+    x0 = to_dev_bits(bits, torch)
+    d, c, _, mc = R.calibrate(to_dev_bits(W.calibration_batch(name)[0], torch))
+    sigma = -1 if mc < 0 else 1
+    nsets = min(64, max(2, int(np.ceil(BUFFER_SETS_MIN_BYTES / (x0.numel() * 2)))))
+    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
+    outs = [(torch.empty((t, n // 2), dtype=torch.uint8, device="cuda"),
+             torch.empty(t, dtype=torch.float32, device="cuda"),
+             torch.empty(t, dtype=torch.float32, device="cuda")) for _ in range(nsets)]
+    stream = torch.cuda.current_stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+
+    def step(i):
+        co, sc, ze = outs[i % nsets]
+        st = L.signrot_rotate_quant_int4_outlier(xs[i % nsets].data_ptr(), t, n, n, c, sigma, co.data_ptr(),
+                                                 sc.data_ptr(), ze.data_ptr(), None, sptr)
+        if st != 0:
+            R.check(st, "signrot_rotate_quant_int4_outlier")
+
+    def cstep(i):
+        co, sc, ze = outs[i % nsets]
+        st = L.signrot_stream_ceiling(xs[i % nsets].data_ptr(), t, n, n, co.data_ptr(), sc.data_ptr(),
+                                      ze.data_ptr(), sptr)
+        if st != 0:
+            R.check(st, "signrot_stream_ceiling")
+
+    ceiling = leg(torch, stream, cstep, warmup, steps)
+    run = leg(torch, stream, step, warmup, steps)
+    bpt = algorithmic_bytes_per_token(n)
+    gbs = bpt * t / (run["mean_ms"] * 1e-3) / 1e9
+    ceil_gbs = bpt * t / (ceiling["mean_ms"] * 1e-3) / 1e9
+    out = {"n": n, "tokens": t, "kernel": R.kernel_name(n), "tokens_per_s": t / (run["mean_ms"] * 1e-3),
+           "launch_ms": run, "achieved_gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS,
+           "ceiling_launch_ms": ceiling, "ceiling_frac_of_peak": ceil_gbs / PEAK_HBM_GBS,
+           "frac_of_ceiling": gbs / ceil_gbs, "input_buffer_sets": nsets,
+           "launches": f"{warmup} warm-up + {steps} timed each, ceiling first"}
+    del xs, outs
+    torch.cuda.empty_cache()
+    return out
 
 
 def to_dev_bits(bits, torch):
