@@ -110,28 +110,43 @@ def algorithmic_bytes_per_token(n: int) -> int:
     return 2 * n + n // 2 + 8
 
 
-def cpu_baseline(bits: np.ndarray, d: np.ndarray) -> dict:
+def cpu_baseline(bits: np.ndarray, d: np.ndarray, per_config: dict | None = None) -> dict:
     """Time the oracle (numpy float64, as it stands) on a bounded sample of the
     same workload: one call over the first tokens of the batch (up to 8192
     at n <= 14336, 2048 above), so the oracle builds its column blocks of H
-    once and the float64 product dominates."""
+    once and the float64 product dominates.  per_config: {name: (first rows
+    of that configuration's batch, its d)}, each timed the same way."""
     import oracle as O
 
+    threads, blas = os.cpu_count() or 1, None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in pools), default=threads)
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in pools})) or None
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+
+    def timed(b, dd):
+        t0 = time.perf_counter()
+        O.rotate_quant_int4(b, dd)
+        return time.perf_counter() - t0
+
     n = bits.shape[1]
     tokens = min(bits.shape[0], 8192 if n <= 14336 else 2048)
-    t0 = time.perf_counter()
-    O.rotate_quant_int4(bits[:tokens], d)
-    dt = time.perf_counter() - t0
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the first {tokens} tokens of the same workload (n={n}) in one oracle call: float64 "
-                      f"dense rotation built from column blocks of H (H construction included) + asymmetric "
-                      f"INT4, {dt:.1f} s"}
+    dt = timed(bits[:tokens], d)
+    out = {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "blas": blas,
+           "sample": f"the first {tokens} tokens of the same workload (n={n}) in one oracle call: float64 "
+                     f"dense rotation built from column blocks of H (H construction included) + asymmetric "
+                     f"INT4, {dt:.1f} s"}
+    if per_config:
+        out["per_config"] = {}
+        for name, (b, dd) in per_config.items():
+            t = timed(b, dd)
+            out["per_config"][name] = {"value": b.shape[0] / t, "unit": "tokens/s", "sample_tokens": b.shape[0],
+                                       "n": b.shape[1], "seconds": t}
+    return out
 
 
 def bench_fold(args, torch, R, W) -> int:
@@ -731,21 +746,29 @@ def main() -> int:
     if not args.no_decode and wname == WORKLOAD and args.tokens is None:
         del xs, outs, calls, dcalls
         torch.cuda.empty_cache()
-        line["other_configs"] = {name: config_leg(R, W, torch, L, name) for name in OTHER_CONFIGS}
+        samples = {}
+        line["other_configs"] = {}
+        for name in OTHER_CONFIGS:
+            line["other_configs"][name], samples[name] = config_leg(R, W, torch, L, name)
+    else:
+        samples = None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy())
+        line["cpu_baseline"] = cpu_baseline(bits, d.cpu().numpy(), samples)
     print(json.dumps(line), flush=True)
     return 0
 
 
 OTHER_CONFIGS = ("n4096_t64", "n8192_t2048", "n14336_t4096", "n28672_t8192")
+# rows of each configuration's batch kept for the oracle's CPU timing
+CPU_SAMPLE_ROWS = {"n4096_t64": 64, "n8192_t2048": 2048, "n14336_t4096": 4096, "n28672_t8192": 1024}
 
 
-def config_leg(R, W, torch, L, name: str, warmup: int = 100, steps: int = 200) -> dict:
+def config_leg(R, W, torch, L, name: str, warmup: int = 100, steps: int = 200):
     """One more configuration on the (c, sigma) entry point: its own synthetic
     batch and calibration, input copies rotated so that each launch reads
     HBM (at most 64 copies: the 64-token batch stays cache-resident and is
-    launch-bound), the traffic-ceiling kernel on the same buffers first."""
+    launch-bound), the traffic-ceiling kernel on the same buffers first.
+    Returns the record and (the batch's first rows, d) for the CPU timing."""
     bits, _ = W.batch(name)
     t, n = bits.shape
     x0 = to_dev_bits(bits, torch)
@@ -785,7 +808,7 @@ def config_leg(R, W, torch, L, name: str, warmup: int = 100, steps: int = 200) -
            "launches": f"{warmup} warm-up + {steps} timed each, ceiling first"}
     del xs, outs
     torch.cuda.empty_cache()
-    return out
+    return out, (np.ascontiguousarray(bits[:CPU_SAMPLE_ROWS[name]]), d.cpu().numpy())
 
 
 def to_dev_bits(bits, torch):
