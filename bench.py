@@ -307,17 +307,17 @@ def bench_linear(args, torch, R, W) -> int:
 
 
 def bench_swiglu(args, torch, R, W) -> int:
-    """The online path with the SwiGLU producer fused in, on the n = 14336
-    law at 8192 tokens: gate and up bf16 [8192, 14336] (seeded synthetic,
-    the massive channel in 20 % of tokens), d calibrated on x of a 256-token
-    calibration batch.  One step = one signrot_swiglu_rotate_quant_int4 call
-    (reads gate and up, writes codes).  Beside it, the unfused pair it
-    replaces: the producer as a library elementwise kernel (torch, binary32
-    SiLU(gate) * up stored as bf16) and then signrot_rotate_quant_int4_outlier
-    on that x."""
-    gate_b, up_b, _ = W.swiglu_batch("n14336_t8192")
+    """The online path with the SwiGLU producer fused in, on the named
+    workload's law (default n = 14336 at 8192 tokens): gate and up bf16
+    [T, n] (seeded synthetic, the massive channel in the workload's outlier
+    tokens), d calibrated on x of a 256-token calibration batch.  One step =
+    one signrot_swiglu_rotate_quant_int4 call (reads gate and up, writes
+    codes).  Beside it, the unfused pair it replaces: the producer as a
+    library elementwise kernel (torch, binary32 SiLU(gate) * up stored as
+    bf16) and then signrot_rotate_quant_int4_outlier on that x."""
+    gate_b, up_b, _ = W.swiglu_batch(args.workload, tokens=args.tokens)
     t, n = gate_b.shape
-    cg, cu, _ = W.swiglu_batch("n14336_t8192", tokens=256, stream=11)
+    cg, cu, _ = W.swiglu_batch(args.workload, tokens=256, stream=11)
     stream = torch.cuda.current_stream()
     g0, u0 = to_dev_bits(gate_b, torch), to_dev_bits(up_b, torch)
     del gate_b, up_b
@@ -368,7 +368,8 @@ def bench_swiglu(args, torch, R, W) -> int:
         "warmup": args.warmup, "ms_per_step": head["wall_s"] * 1e3 / args.steps, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"gate, up bf16 [{t} x {n}] (gate N(0,1.5), up N(0,0.6); massive channel {c} "
-                               "in 20% of tokens), x = bf16(SiLU(gate) * up) in the kernel",
+                               f"in {100 * W.WORKLOADS[args.workload].p_outlier:.0f}% of tokens), "
+                               "x = bf16(SiLU(gate) * up) in the kernel",
                    "kernel": R.kernel_name(n) + " (SwiGLU instance)",
                    "launch_ms": {k: head[k] for k in ("mean_ms", "p10_ms", "p50_ms", "p90_ms", "group")},
                    "unfused_producer_ms": unf_prod["mean_ms"],
