@@ -14,9 +14,10 @@
 //   staging: HBM -> VGPRs (16-byte loads issued one row ahead) -> LDS,
 //     transposed: b-row b holds x[0..m-1][b] in bf16 with a contiguous,
 //     zero-padded to 32 KC entries, at LDS row rho(b) (the four lane bits of b
-//     low, its tile bits high) with a pitch of 64 KC + 16 bytes, so that the
-//     16 lanes of an operand read cover 16 distinct bank groups.  Two a-rows
-//     are staged together so that every LDS write is a whole dword.
+//     low, its tile bits high) with a pitch of 64 KC + 32 bytes (64 KC + 16
+//     where the wider rows would cost a resident work-group, and with 16
+//     column tiles; see OuterShape::RS).  Two a-rows are staged together so
+//     that every LDS write is a whole dword.
 //   stage 1 (MFMA): Z[a'][b] = sum_a W[a'][a] x[a][b], W = H_m^T (each row
 //     a' times sigma * H_m[c_a][a'] for the calibrated sign vector), as
 //     v_mfma_f32_16x16x32_bf16 with M = a' (16 per tile), K = a (32 per
@@ -61,15 +62,34 @@ struct OuterShape {
   static_assert(KC >= 1 && KC <= 16, "outer order up to 512");
   static constexpr int KB = 4 + LGN;          // log2 B
   static constexpr int B = 16 * NTL;
-  static constexpr int RS = 64 * KC + 16;     // LDS bytes per b-row
+  // LDS bytes per b-row.  An operand read serves 32 lanes (16 b-rows, two
+  // 16-byte chunks) per pass in 8-byte halves.  On gfx950 that was 2-way bank
+  // conflicted with a 64 KC + 16 pitch (rocprofv3 SQ_LDS_BANK_CONFLICT: 4
+  // cycles per read, 8.0e6 per launch at n = 11008 x 8192) and is conflict-free
+  // with 64 KC + 32 (1.4e5, what is left coming from other accesses); the
+  // counts fit 64 banks of 8 bytes.  The staging writes then conflict more
+  // (1.4e6 -> 4.2e6 there); the launch is 1-8 % faster at most widths with
+  // 2^k <= 128 (384 and 8832 ran 1-3 % slower).
+  // The wider pitch is not used where it would leave room for fewer
+  // work-groups per CU (n = 9216 ran 81 -> 135 us, 5632 34 -> 38 us) nor with
+  // 16 column tiles, where it measured slower (n = 27648, 17408, 5120).
+  static constexpr int kMaxN = 32 * KC * B;
+  // waves per work-group for m <= 32 KC: ceil(ceil(m / 16) / MTW)
+  static constexpr int kMaxWaves = (2 * KC + MTW - 1) / MTW;
+  // work-groups per CU that the LDS (160 KiB) leaves room for at pitch rs,
+  // capped by 32 waves per CU
+  static constexpr int lds_bytes(int rs) { return 2 * B * rs + 4 * (kMaxN / 32) + 280; }  // + d bits, reductions
+  static constexpr int wgs_per_cu(int rs) {
+    const int by_lds = 163840 / ((lds_bytes(rs) + 511) / 512 * 512);
+    return by_lds < 32 / kMaxWaves ? by_lds : 32 / kMaxWaves;
+  }
+  static constexpr bool kWidePitch = NTL <= 8 && wgs_per_cu(64 * KC + 32) == wgs_per_cu(64 * KC + 16);
+  static constexpr int RS = 64 * KC + (kWidePitch ? 32 : 16);
   static constexpr int kBufBytes = B * RS;
   static constexpr int NV = MTW * NTL * 4;    // values per lane
   // staging units (two 16-byte loads: 8 channels of a-rows 2p and 2p + 1)
   // per thread: m NTL units over 64 ceil(m / (16 MTW)) threads
   static constexpr int UPT = (NTL * MTW + 3) / 4;
-  static constexpr int kMaxN = 32 * KC * B;
-  // waves per work-group for m <= 32 KC: ceil(ceil(m / 16) / MTW)
-  static constexpr int kMaxWaves = (2 * KC + MTW - 1) / MTW;
   static_assert(kMaxWaves <= 16, "at most 16 waves per work-group");
 };
 
