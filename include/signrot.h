@@ -376,7 +376,9 @@ int signrot_outer_fold(int64_t n);
  *                    (11008, 13824, 18944, 8960, 27648, 5120, 5504, 896,
  *                    1792 among them), and widths that reach such a shape
  *                    with Sylvester bits moved into the outer factor (24576,
- *                    20480, 12288, 10240, 6144, 64 .. 2048, 32768);
+ *                    20480, 12288, 10240, 6144, 64 .. 2048, 32768; most
+ *                    2^k = 256 widths, e.g. 5120 and 17408, run as
+ *                    (2 m) * 128);
  *   "rq_generic"     every other supported n.
  * Host-only (no GPU needed). */
 const char* signrot_kernel_name(int64_t n);

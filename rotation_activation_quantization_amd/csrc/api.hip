@@ -120,8 +120,13 @@ const uint32_t* outer_mask_device(int m, hipError_t* err, hipStream_t stream, bo
 // The rotate kernel for a shape: the 28 * 2^k / 2^k MFMA kernels, the
 // outer-order MFMA kernel, or the generic one.  The outer-order kernel also
 // takes n = m 2^k read as (m 2^fold) 2^(k - fold): the same H with fold
-// Sylvester index bits moved into its outer factor, for 2^k beyond its
-// table (2^k > 256) or a Sylvester width without a fast kernel.
+// Sylvester index bits moved into its outer factor, for 2^k >= 256 or a
+// Sylvester width without a fast kernel.  2^(k - fold) = 128 comes first,
+// then 256 (fold 0 when 2^k = 256), 32, 64, 16.  Measured at 8192 tokens, a
+// 2^k = 256 width read with 128 columns ran 1.1-1.9x faster (3072, 5120,
+// 13312-21504), except where that reading has 3 K chunks (65 <= 2m <= 96):
+// 9216 and 11264 ran 11 % slower.  Such a plan is therefore taken only when
+// no later one fits.
 enum class RqKernel { kFast, kOuter, kGeneric };
 struct RqPlan {
   RqKernel kind;
@@ -130,15 +135,22 @@ struct RqPlan {
 
 RqPlan rq_plan_for(const Shape& sh) {
   if (rq_fast_supports(sh.n, sh.k, sh.m28)) return {RqKernel::kFast, 0};
-  if (rq_outer_supports(sh.m, sh.k)) return {RqKernel::kOuter, 0};
-  if (sh.m == 1 || (sh.m != 28 && sh.k > 8)) {
-    // 2^(k - fold) = 128 first (the kernel's best column-tile count), then 256, 32, 64, 16
+  if (sh.k != 8 && rq_outer_supports(sh.m, sh.k)) return {RqKernel::kOuter, 0};
+  if (sh.m == 1 || (sh.m != 28 && sh.k >= 8)) {
+    RqPlan kept{RqKernel::kGeneric, 0};
     for (const int kk : {7, 8, 5, 6, 4}) {
       const int fold = sh.k - kk;
-      const int64_t mm = static_cast<int64_t>(sh.m) << (fold > 0 ? fold : 0);
-      if (fold >= (sh.m == 1 ? 2 : 1) && mm <= kMaxOuter && rq_outer_supports(static_cast<int>(mm), kk))
-        return {RqKernel::kOuter, fold};
+      if (fold < (sh.m == 1 ? 2 : 0)) continue;
+      const int64_t mm = static_cast<int64_t>(sh.m) << fold;
+      if (mm > kMaxOuter || !rq_outer_supports(static_cast<int>(mm), kk)) continue;
+      const RqPlan p{RqKernel::kOuter, fold};
+      if (kk == 7 && (mm + 31) / 32 == 3) {
+        if (kept.kind == RqKernel::kGeneric) kept = p;
+        continue;
+      }
+      return p;
     }
+    return kept;
   }
   return {RqKernel::kGeneric, 0};
 }

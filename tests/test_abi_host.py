@@ -384,9 +384,13 @@ def test_folded_outer_factor_equals_kronecker_of_oracle_factors(m, fold):
 
 
 def test_fold_choice_for_wide_widths(L):
-    """The fold the rotate kernel takes: 2^(k - fold) = 128 first, then 256."""
-    want = {24576: 4, 20480: 3, 12288: 3, 10240: 2, 6144: 2, 32768: 7, 2048: 4, 1024: 3, 512: 2, 256: 3, 128: 2,
-            11008: 0, 14336: 0, 4096: 0, 22016: 0}
+    """The fold the rotate kernel takes: 2^(k - fold) = 128 first, then 256,
+    except that a 128-column reading with 3 K chunks (outer order 65..96)
+    gives way to the 256-column one (12288, 10240, and 9216 and 11264 at
+    their own order)."""
+    want = {24576: 4, 20480: 3, 12288: 2, 10240: 1, 6144: 2, 32768: 7, 2048: 4, 1024: 3, 512: 2, 256: 3, 128: 2,
+            11008: 0, 14336: 0, 4096: 0, 22016: 0, 3072: 1, 5120: 1, 17408: 1, 21504: 1, 9216: 0, 11264: 0,
+            25600: 0, 27648: 0}
     for n, f in want.items():
         assert R.outer_fold(n) == f, n
     assert R.outer_fold(6) == -1

@@ -32,14 +32,16 @@ pytestmark = pytest.mark.gpu
 # MLP widths of common models (11008, 13824, 18944) plus two-factor widths
 WIDTHS = [12, 20, 24, 40, 72, 344, 1000, 2560, 4864, 5120, 5632, 8960, 11008, 13824, 17408, 18944, 24576, 27648]
 CHEAP = [n for n in WIDTHS if n <= 8960]
-# widths read with Sylvester bits moved into the outer factor (2^k > 256, or
-# a Sylvester width without its own kernel): n -> (outer order, 2^k) the
+# widths read with Sylvester bits moved into the outer factor (2^k >= 256,
+# or a Sylvester width without its own kernel): n -> (outer order, 2^k) the
 # MFMA kernel sees
 FOLDED = {64: (4, 16), 128: (4, 32), 256: (8, 32), 512: (4, 128), 1024: (8, 128), 2048: (16, 128), 6144: (48, 128),
-          10240: (80, 128), 12288: (96, 128), 20480: (160, 128), 24576: (192, 128), 32768: (128, 256)}
+          10240: (40, 256), 12288: (48, 256), 20480: (160, 128), 24576: (192, 128), 32768: (128, 256),
+          # 2^k = 256 read with 128 columns (not where that reading has 3 K chunks: 9216, 11264)
+          3072: (24, 128), 5120: (40, 128), 13312: (104, 128), 17408: (136, 128), 21504: (168, 128)}
 # the kernel each width runs: (K chunks, column tiles) of the MFMA kernel's table
-OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5120: (1, 16), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
-              13824: (4, 8), 17408: (3, 16), 18944: (5, 8), 27648: (4, 16)}
+OUTER_MFMA = {2560: (1, 8), 4864: (3, 4), 5632: (2, 8), 8960: (5, 4), 11008: (11, 2),
+              13824: (4, 8), 18944: (5, 8), 27648: (4, 16)}
 
 
 def say(msg):
@@ -219,7 +221,7 @@ def test_full_size_workload_sampled():
 
 # one width per shape of the MFMA kernel's table not covered above:
 # (K chunks, column tiles) -> n
-MORE_SHAPES = {(1, 2): 384, (1, 4): 768, (1, 16): 3072, (2, 2): 1152, (2, 4): 2304, (2, 16): 9216, (3, 2): 2176,
+MORE_SHAPES = {(1, 2): 384, (1, 4): 768, (2, 2): 1152, (2, 4): 2304, (2, 16): 9216, (3, 2): 2176,
                (3, 8): 8704, (4, 2): 3200, (4, 4): 6400, (5, 2): 4224, (6, 2): 5248, (6, 4): 10496, (6, 8): 20992,
                (7, 2): 6272, (7, 4): 12544, (8, 2): 7296, (8, 4): 14592, (9, 2): 8832, (10, 2): 9600, (12, 2): 11648,
                # one column tile (2^k = 16): 5504 = 344 * 16 is half of 11008
