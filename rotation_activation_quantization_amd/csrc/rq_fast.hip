@@ -45,8 +45,10 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "rq_fast_common.h"
+
 
 namespace signrot {
 namespace {
@@ -193,10 +195,28 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int chan0 = (ap << KB) + 4 * NT * outm;  // first of this lane's channels
   const uint32_t dword = general ? (dbits[chan0 >> 5] >> (chan0 & 31)) : 0u;
 
-  const int64_t tokens = a.tokens;
-  const int64_t grid = gridDim.x;
+  // Row indices fit in 32 bits: the launcher splits larger calls.
+  const int tokens = static_cast<int>(a.tokens);
+  const int grid = static_cast<int>(gridDim.x);
 
-  auto write_row = [&](uint32_t bo, int xslot) {
+  // LDS byte offsets kept for the whole loop, so that the buffer and the K
+  // chunk enter the LDS instructions as immediate offsets: the operand read
+  // of tile t at taddr[t], the staging write of chunk unit i, half h at
+  // waddr[i][h] (both in buffer 0).
+  uint32_t taddr[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) taddr[t] = rbase ^ (S::KMUL * static_cast<uint32_t>(t));
+  uint32_t waddr[S::CPT][2];
+#pragma unroll
+  for (int i = 0; i < S::CPT; ++i) {
+    waddr[i][0] = unit_l(i) + wl[0];
+    waddr[i][1] = unit_l(i) + wl[1];
+  }
+
+  // Stage the row held in st into buffer BO (0 or kRowBytes).
+  auto write_row = [&](auto boc) {
+    constexpr uint32_t BO = decltype(boc)::value;
+    constexpr int XSLOT = BO ? 1 : 0;
     if constexpr (SWIGLU) {
 #pragma unroll
       for (int i = 0; i < S::CPT; ++i) st[i] = swiglu_chunk(st[i], stu[i]);
@@ -210,52 +230,80 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
           if (q != (xc_e >> 1)) continue;
           const uint32_t word = st[i][q];
           const int hi = xc_e & 1;
-          xcl[xslot] = __uint_as_float(hi ? (word & 0xffff0000u) : (word << 16));
+          xcl[XSLOT] = __uint_as_float(hi ? (word & 0xffff0000u) : (word << 16));
           st[i][q] = hi ? (word & 0x0000ffffu) : (word & 0xffff0000u);
         }
       }
     }
 #pragma unroll
     for (int i = 0; i < S::CPT; ++i) {
-      uint8_t* base = lds + (bo + unit_l(i));
-      *reinterpret_cast<uint2*>(base + wl[0]) = make_uint2(st[i][0], st[i][1]);
-      *reinterpret_cast<uint2*>(base + wl[1]) = make_uint2(st[i][2], st[i][3]);
+      *reinterpret_cast<uint2*>(lds + waddr[i][0] + BO) = make_uint2(st[i][0], st[i][1]);
+      *reinterpret_cast<uint2*>(lds + waddr[i][1] + BO) = make_uint2(st[i][2], st[i][3]);
     }
   };
+  using Buf0 = std::integral_constant<uint32_t, 0u>;
+  using Buf1 = std::integral_constant<uint32_t, static_cast<uint32_t>(S::kRowBytes)>;
 
   // Rows by grid stride: cur (in the LDS buffer), nxt (loads in flight),
   // nn (loaded while cur is processed).
-  int64_t cur = blockIdx.x;
-  int64_t nxt = cur + grid;
-  int64_t nn = nxt + grid;
+  int cur = blockIdx.x;
+  int nxt = cur + grid;
+  int nn = nxt + grid;
   if (cur >= tokens) return;
   wait_vmcnt<0>();
-  write_row(0u, 0);
+  write_row(Buf0{});
   if (nxt < tokens) load_row(nxt);
   lds_barrier();
+  bool first = true;
 
-  for (int it = 0; cur < tokens; ++it) {
-    const int64_t row = cur;
-    const int par = it & 1;
-    const uint32_t bo = par ? static_cast<uint32_t>(S::kRowBytes) : 0u;
+  // One row from buffer PAR (a compile-time constant: the loop below runs the
+  // two buffers in turn).
+  auto row_step = [&](auto parc) {
+    constexpr int PAR = decltype(parc)::value;
+    constexpr uint32_t BO = PAR ? static_cast<uint32_t>(S::kRowBytes) : 0u;
+    const int row = cur;
+    const uint64_t urow = static_cast<uint32_t>(row);  // (64-bit offsets from a uniform row)
 
     // (1) MFMA stage from this row's buffer
     float v[NV];
-    {
-      const uint32_t base = rbase + bo;
+    // Operands of tile t + 1 are read while tile t's MFMAs run (pinned by the
+    // scheduling groups below), so the LDS latency overlaps the MFMAs.  The
+    // SwiGLU instances other than the order-28 one without y_out read tile by
+    // tile instead: they have no registers to spare.
+    constexpr bool kPipe = !SWIGLU || (KA == 28 && !YOUT);
+    u32x4_t bq[2][S::NKC];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint8_t* tp = lds + (base ^ (S::KMUL * t));
-        f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        u32x4_t b[S::NKC];
+    for (int kc = 0; kc < S::NKC; ++kc)
+      bq[0][kc] = *reinterpret_cast<const u32x4_t*>(lds + taddr[0] + BO + 4 * S::PB * kc);
 #pragma unroll
-        for (int kc = 0; kc < S::NKC; ++kc) b[kc] = *reinterpret_cast<const u32x4_t*>(tp + 4 * S::PB * kc);
+    for (int t = 0; t < NT; ++t) {
+      const int cb_ = kPipe ? (t & 1) : 0;
+      if (t + 1 < NT && kPipe) {
 #pragma unroll
         for (int kc = 0; kc < S::NKC; ++kc)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[kc], __builtin_bit_cast(bf16x8_t, b[kc]), acc, 0, 0, 0);
+          bq[cb_ ^ 1][kc] = *reinterpret_cast<const u32x4_t*>(lds + taddr[t + 1] + BO + 4 * S::PB * kc);
+      } else if (t > 0 && !kPipe) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[4 * t + r] = acc[r];
+        for (int kc = 0; kc < S::NKC; ++kc)
+          bq[0][kc] = *reinterpret_cast<const u32x4_t*>(lds + taddr[t] + BO + 4 * S::PB * kc);
       }
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < S::NKC; ++kc)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wA[kc], __builtin_bit_cast(bf16x8_t, bq[cb_][kc]), acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[4 * t + r] = acc[r];
+    }
+    if constexpr (kPipe) {
+      // tile 0's reads, then (tile t + 1's reads, tile t's MFMAs), then the
+      // last tile's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, S::NKC, 0);
+#pragma unroll
+      for (int t = 0; t + 1 < NT; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x100, S::NKC, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, S::NKC, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, S::NKC, 0);
     }
 
     // (2) stage the next row into the other buffer; start loading the one after
@@ -263,12 +311,14 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       // The loads were issued a row ago; after them every wave issued the
       // previous row's code store (plus NT y stores with y_out); wave 0 also
       // scale and zero, so the same count only makes it wait longer.
-      if (it == 0) wait_vmcnt<0>();
+      if (first) wait_vmcnt<0>();
       else if (YOUT) wait_vmcnt<1 + NT>();
       else wait_vmcnt<1>();
-      write_row(bo ^ static_cast<uint32_t>(S::kRowBytes), par ^ 1);
+      if constexpr (PAR) write_row(Buf0{});
+      else write_row(Buf1{});
       if (nn < tokens) load_row(nn);
     }
+    first = false;
 
     // (3) NQ-point transform over the quad index
     reg_stage<NT, 0>(v);
@@ -291,23 +341,26 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     }
 
     // (4) min / max over the row: lanes, then waves through LDS
-    float mn = v[0], mx = v[0];
+    float mn = min3_of(v[0], v[1], v[2]);
+    float mx = max3_of(v[0], v[1], v[2]);
 #pragma unroll
-    for (int e = 1; e + 1 < NV; e += 2) {
+    for (int e = 3; e + 1 < NV; e += 2) {
       min3_acc(mn, v[e], v[e + 1]);
       max3_acc(mx, v[e], v[e + 1]);
     }
-    mn = fmin_raw(mn, v[NV - 1]);
-    mx = fmax_raw(mx, v[NV - 1]);
+    if constexpr (NV % 2 == 0) {
+      mn = fmin_raw(mn, v[NV - 1]);
+      mx = fmax_raw(mx, v[NV - 1]);
+    }
     wave_minmax(mn, mx);
-    float* rd = red + 32 * par;  // per-wave min at rd[w], max at rd[16 + w]
+    float* rd = red + 32 * PAR;  // per-wave min at rd[w], max at rd[16 + w]
     if (lane == 63) {
       rd[w] = mn;
       rd[16 + w] = mx;
     }
     // x_c of this row, read before the barrier: the previous barrier published
     // it, and its slot is next written (for the row after next) after this one
-    const float xc = general ? 0.0f : xcl[par];
+    const float xc = general ? 0.0f : xcl[PAR];
     lds_barrier();
 #pragma unroll
     for (int q = 0; q < S::kWaves; q += 4) {
@@ -359,7 +412,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       }
       q[u] = ev | (od << 4);
     }
-    const __amdgpu_buffer_rsrc_t cs = buffer_rsrc(a.codes + row * static_cast<int64_t>(S::N / 2), S::N / 2);
+    const __amdgpu_buffer_rsrc_t cs = buffer_rsrc(a.codes + urow * (S::N / 2), S::N / 2);
     const uint32_t coff = static_cast<uint32_t>(chan0 / 2);
     if constexpr (NT == 8) {
       store_b128_held<kNontemporal>(u32x4_t{q[0], q[1], q[2], q[3]}, cs, coff, 0);
@@ -369,7 +422,7 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
       __builtin_amdgcn_raw_buffer_store_b32(q[0], cs, coff, 0, kNontemporal);
     }
     if (YOUT) {
-      float* yp = a.yout + row * static_cast<int64_t>(S::N) + chan0;
+      float* yp = a.yout + urow * S::N + chan0;
 #pragma unroll
       for (int e4 = 0; e4 < NT; ++e4) {
         f32x4_t o;
@@ -383,6 +436,12 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
     cur = nxt;
     nxt = nn;
     nn += grid;
+  };
+  for (;;) {
+    row_step(std::integral_constant<int, 0>{});
+    if (cur >= tokens) break;
+    row_step(std::integral_constant<int, 1>{});
+    if (cur >= tokens) break;
   }
   wait_vmcnt<0>();
 }
@@ -422,7 +481,31 @@ void rq_fast_kernel(RqArgs a) {
 }
 
 template <int KA, int KB>
+hipError_t launch_shape_rows(const RqArgs& a, hipStream_t stream);
+
+// The kernel keeps row indices in 32 bits: calls of more than 2^30 rows run
+// as consecutive launches over slices of the batch.
+template <int KA, int KB>
 hipError_t launch_shape(const RqArgs& a, hipStream_t stream) {
+  constexpr int64_t kMaxRows = int64_t{1} << 30;
+  if (a.tokens <= kMaxRows) return launch_shape_rows<KA, KB>(a, stream);
+  for (int64_t r0 = 0; r0 < a.tokens; r0 += kMaxRows) {
+    RqArgs s = a;
+    s.tokens = (a.tokens - r0 < kMaxRows) ? a.tokens - r0 : kMaxRows;
+    s.x = a.x + r0 * a.ld;
+    if (a.x2) s.x2 = a.x2 + r0 * a.ld;
+    s.codes = a.codes + r0 * (a.n / 2);
+    s.scale = a.scale + r0;
+    s.zero = a.zero + r0;
+    if (a.yout) s.yout = a.yout + r0 * a.n;
+    const hipError_t e = launch_shape_rows<KA, KB>(s, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int KA, int KB>
+hipError_t launch_shape_rows(const RqArgs& a, hipStream_t stream) {
   using S = FastShape<KA, KB>;
   // resident workgroups per CU (registers and LDS), asked once per shape
   // (computed by any thread that finds 0; all compute the same value)
