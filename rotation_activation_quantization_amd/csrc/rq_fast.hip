@@ -53,6 +53,18 @@
 namespace signrot {
 namespace {
 
+// min(x, y, z) and max(x, y, z) as single v_min3 / v_max3 ops
+__device__ __forceinline__ float min3_of(float x, float y, float z) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+__device__ __forceinline__ float max3_of(float x, float y, float z) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
 // MAYBE_GENERAL: d arrived as a vector and may lack the calibrated form; the
 // body then takes `general` (a wave-uniform flag) at run time, so that both
 // cases share one register allocation.  Without it d is given as (c, sigma).

@@ -130,18 +130,6 @@ __device__ __forceinline__ void max3_acc(float& acc, float x, float y) {
   asm("v_max3_f32 %0, %0, %1, %2" : "+v"(acc) : "v"(x), "v"(y));
 }
 
-// min(x, y, z) and max(x, y, z) as single v_min3/v_max3 ops
-__device__ __forceinline__ float min3_of(float x, float y, float z) {
-  float r;
-  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-  return r;
-}
-__device__ __forceinline__ float max3_of(float x, float y, float z) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
-  return r;
-}
-
 // Plain v_min_f32 / v_max_f32.  fminf / fmaxf make the compiler quiet NaN
 // inputs with an extra v_max_f32 x, x, x on every operand it cannot prove
 // canonical (DPP results, LDS loads); the inputs here are finite.
