@@ -109,10 +109,8 @@ __device__ inline DForm decode_d_form(const RqArgs& a, const uint32_t* dbits, in
 }
 
 // Sign bits (bit set when the byte is negative) of 32 consecutive int8
-// entries d[32 w .. 32 w + 31], read as two 16-byte loads.
-__device__ __forceinline__ uint32_t sign_word(const int8_t* d32) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(d32);
-  const uint4 hi = *reinterpret_cast<const uint4*>(d32 + 16);
+// entries, given as their two 16-byte halves.
+__device__ __forceinline__ uint32_t sign_word_of(const uint4& lo, const uint4& hi) {
   const uint32_t q[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   uint32_t word = 0u;
 #pragma unroll
@@ -124,6 +122,11 @@ __device__ __forceinline__ uint32_t sign_word(const int8_t* d32) {
   return word;
 }
 
+// The same for d[32 w .. 32 w + 31], read as two 16-byte loads.
+__device__ __forceinline__ uint32_t sign_word(const int8_t* d32) {
+  return sign_word_of(*reinterpret_cast<const uint4*>(d32), *reinterpret_cast<const uint4*>(d32 + 16));
+}
+
 // Builds the d bitmask in LDS (n / 32 words; needs n % 32 == 0 and d 16-byte
 // aligned) with every thread of the block.
 __device__ inline void build_dbits(const int8_t* d, int n, uint32_t* dbits) {
@@ -132,9 +135,12 @@ __device__ inline void build_dbits(const int8_t* d, int n, uint32_t* dbits) {
 
 // Same decision as decode_d_form, in parallel, for k >= 5 (a 32-bit word of
 // the mask then lies inside one block of 2^k channels).  h28 holds the row
-// masks of H28 in LDS.  Every thread of the block must call it.
+// masks of H28 in LDS.  Every thread of the block must call it.  THREADS: the
+// block size when the caller knows it at compile time (else 0: blockDim.x).
+template <int THREADS = 0>
 __device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbits, const uint32_t* h28,
                                            int* sh_scratch) {
+  const int nthreads = THREADS > 0 ? THREADS : static_cast<int>(blockDim.x);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   auto dbit = [&](int j) -> uint32_t { return (dbits[j >> 5] >> (j & 31)) & 1u; };
@@ -161,11 +167,11 @@ __device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbit
       sh_scratch[0] = found;
       sh_scratch[1] = (ca << a.k) | cb;
       sh_scratch[2] = static_cast<int>(d0 ^ (a.m28 ? (h28[ca] & 1u) : 0u));
+      sh_scratch[3] = 0;  // set by any thread that finds an entry off the form
     }
   }
   __syncthreads();
   DForm f{sh_scratch[0], sh_scratch[1], sh_scratch[2]};
-  int bad = 0;
   if (f.structured) {
     const int bmask = (1 << a.k) - 1;
     const int cb = f.c & bmask;
@@ -174,16 +180,18 @@ __device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbit
     uint32_t pw = 0u;
 #pragma unroll
     for (int i = 0; i < 32; ++i) pw |= (__popc(static_cast<uint32_t>(cb & i)) & 1u) << i;
-    for (int w = tid; w < a.n / 32; w += blockDim.x) {
+    for (int w = tid; w < a.n / 32; w += nthreads) {
       const int j0 = 32 * w;
       uint32_t flip = static_cast<uint32_t>(f.neg) ^ (__popc(static_cast<uint32_t>(cb & j0 & bmask)) & 1u);
       if (a.m28) flip ^= (h28[ca] >> (j0 >> a.k)) & 1u;
       const uint32_t want = flip ? ~pw : pw;
-      bad |= static_cast<int>(dbits[w] != want);
+      if (dbits[w] != want) sh_scratch[3] = 1;  // every writer stores the same value
     }
   }
-  bad = __syncthreads_or(bad);
-  if (bad) f.structured = 0;
+  // (a plain flag in LDS rather than __syncthreads_or, whose group-size
+  // lookup waits for every outstanding global load)
+  __syncthreads();
+  if (sh_scratch[3]) f.structured = 0;
   if (!f.structured) {
     f.c = -1;
     f.neg = 0;

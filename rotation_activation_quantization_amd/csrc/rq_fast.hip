@@ -68,11 +68,12 @@ __device__ __forceinline__ float max3_of(float x, float y, float z) {
 // MAYBE_GENERAL: d arrived as a vector and may lack the calibrated form; the
 // body then takes `general` (a wave-uniform flag) at run time, so that both
 // cases share one register allocation.  Without it d is given as (c, sigma).
-template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false, bool SWIGLU = false>
+// get_form() yields the form of d; every thread calls it once, after the
+// first row's loads have been issued.
+template <int KA, int KB, bool MAYBE_GENERAL, bool YOUT, bool ZINT = false, bool SWIGLU = false, class GetForm>
 __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbits, const uint32_t* h28,
-                             const DForm& form, float* red, float* xcl) {
+                             GetForm get_form, float* red, float* xcl) {
   using S = FastShape<KA, KB>;
-  const bool general = MAYBE_GENERAL && __builtin_amdgcn_readfirstlane(form.structured) == 0;
   constexpr int NT = S::NT;
   constexpr int NV = S::NV;
   const int tid = threadIdx.x;
@@ -80,14 +81,6 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4;
   const int nl = lane & 15;
-
-  const int c = general ? 0 : __builtin_amdgcn_readfirstlane(form.c);
-  const int ca = c >> KB;
-  const int cb = c & ((1 << KB) - 1);
-  const int cbb = cb & 3;
-  const int cbq_lo = (cb >> 2) & (NT - 1);
-  const int cbq_hi = cb >> (2 + S::LG);
-  const int sig = (!general && __builtin_amdgcn_readfirstlane(form.neg)) ? -1 : 1;
 
   // Staging: chunk unit s = w + W i (i < CPT) of 64 chunks; lane L takes the
   // a-row of parity L & 1 and chunk index e = L >> 1 inside the unit.  With
@@ -131,21 +124,40 @@ __device__ void rq_fast_body(const RqArgs& a, uint8_t* lds, const uint32_t* dbit
   // Row loads through a buffer resource on the row (scalar base, the
   // wave-uniform unit offset as the scalar offset, the lane offset gl), so no
   // per-lane 64-bit address is kept across the loop.
-  auto load_row = [&](int64_t r) {
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.x + r * a.ld, 2u * S::N);
+  // (bytes < 2 n: a row past the batch, read as zeros without a memory access)
+  auto load_row = [&](int64_t r, uint32_t bytes = 2u * S::N) {
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(a.x + r * a.ld, bytes);
 #pragma unroll
     for (int i = 0; i < S::CPT; ++i)
       st[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, gl, unit_g(i), kNontemporal));
     if constexpr (SWIGLU) {
-      const __amdgpu_buffer_rsrc_t ru = buffer_rsrc(a.x2 + r * a.ld, 2u * S::N);
+      const __amdgpu_buffer_rsrc_t ru = buffer_rsrc(a.x2 + r * a.ld, bytes);
 #pragma unroll
       for (int i = 0; i < S::CPT; ++i)
         stu[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ru, gl, unit_g(i), kNontemporal));
     }
   };
-  // The first row's loads go out before the weights are built, so their
-  // latency overlaps the set-up; that matters most for a few tokens per call.
-  if (static_cast<int64_t>(blockIdx.x) < a.tokens) load_row(blockIdx.x);
+  // The first row's loads go out before the sign vector's form is known and
+  // before the weights are built, so their latency overlaps the set-up
+  // (reading and decoding d included: a workgroup barrier does not wait for
+  // global loads); that matters most for a few tokens per call.  The launch
+  // has at most one work-group per row.  When d is decoded here, the loads are
+  // issued on every path, so that the compiler's memory-counter wait for d's
+  // earlier loads can count them as outstanding.
+  if constexpr (MAYBE_GENERAL)
+    load_row(blockIdx.x, static_cast<int64_t>(blockIdx.x) < a.tokens ? 2u * S::N : 0u);
+  else if (static_cast<int64_t>(blockIdx.x) < a.tokens)
+    load_row(blockIdx.x);
+
+  const DForm form = get_form();
+  const bool general = MAYBE_GENERAL && __builtin_amdgcn_readfirstlane(form.structured) == 0;
+  const int c = general ? 0 : __builtin_amdgcn_readfirstlane(form.c);
+  const int ca = c >> KB;
+  const int cb = c & ((1 << KB) - 1);
+  const int cbb = cb & 3;
+  const int cbq_lo = (cb >> 2) & (NT - 1);
+  const int cbq_hi = cb >> (2 + S::LG);
+  const int sig = (!general && __builtin_amdgcn_readfirstlane(form.neg)) ? -1 : 1;
 
   // MFMA weights, A operand: lane (g, nl) holds A[m = nl][k = 8 g + i] with
   // m -> (a' = 4 w + (nl >> 2), c = nl & 3), k -> (a = 8 kc + 2 g + (i >> 2), bb = i & 3).
@@ -479,17 +491,35 @@ void rq_fast_kernel(RqArgs a) {
       *reinterpret_cast<u32x4_t*>(lds + 2 * S::kRowBytes + o) = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  DForm form;
   if constexpr (!DVEC) {
-    // d = sigma * (row c of H) by construction: nothing to read or decode
-    __syncthreads();
-    form = DForm{1, a.form_c, a.form_neg};
+    // d = sigma * (row c of H) by construction: nothing to read or decode;
+    // the barrier publishes h28_lds and the zeroed rows
+    rq_fast_body<KA, KB, false, YOUT, ZINT, SWIGLU>(
+        a, lds, dbits, h28_lds,
+        [&] {
+          __syncthreads();
+          return DForm{1, a.form_c, a.form_neg};
+        },
+        red, xcl);
   } else {
-    build_dbits(a.d, a.n, dbits);  // bit j set when d_j = -1
-    __syncthreads();
-    form = decode_d_form_fast(a, dbits, h28_lds, scratch);
+    // This thread's first 32 entries of d are read before the body issues the
+    // first row's loads, so that the decode waits for them alone.
+    constexpr int kWords = S::N / 32;
+    const int8_t* d32 = a.d + 32 * (tid < kWords ? tid : 0);
+    const uint4 dlo = *reinterpret_cast<const uint4*>(d32);
+    const uint4 dhi = *reinterpret_cast<const uint4*>(d32 + 16);
+    __builtin_amdgcn_sched_barrier(0);  // keep them ahead of the row's loads
+    rq_fast_body<KA, KB, true, YOUT, ZINT, SWIGLU>(
+        a, lds, dbits, h28_lds,
+        [&] {
+          // the bitmask of d in LDS, bit j set when d_j = -1
+          if (tid < kWords) dbits[tid] = sign_word_of(dlo, dhi);
+          for (int wd = tid + S::kThreads; wd < kWords; wd += S::kThreads) dbits[wd] = sign_word(a.d + 32 * wd);
+          __syncthreads();
+          return decode_d_form_fast<S::kThreads>(a, dbits, h28_lds, scratch);
+        },
+        red, xcl);
   }
-  rq_fast_body<KA, KB, DVEC, YOUT, ZINT, SWIGLU>(a, lds, dbits, h28_lds, form, red, xcl);
 }
 
 template <int KA, int KB>
