@@ -480,10 +480,18 @@ void rq_fast_kernel(RqArgs a) {
   __shared__ __attribute__((aligned(16))) float red[64];
   __shared__ float xcl[2];
   __shared__ int scratch[4];
-  __shared__ uint32_t h28_lds[28];
+  __shared__ __attribute__((aligned(16))) uint32_t h28_lds[28];
   const int tid = threadIdx.x;
-  if (tid < 28) h28_lds[tid] = a.h28mask[tid];
   if constexpr (KA == 28) {
+    // The H28 row masks are kernel arguments: read with constant offsets they
+    // are scalar loads, so no wait on the vector memory counter (which would
+    // also wait for the first row's loads) comes before the row is requested.
+    if (tid == 0) {
+#pragma unroll
+      for (int q = 0; q < 7; ++q)
+        *reinterpret_cast<u32x4_t*>(h28_lds + 4 * q) =
+            u32x4_t{a.h28mask[4 * q], a.h28mask[4 * q + 1], a.h28mask[4 * q + 2], a.h28mask[4 * q + 3]};
+    }
     // zero the second buffer's first two pair-rows and the two rows behind it
     // (read with zero weights before any row has been staged there)
     for (int o = 16 * tid; o < 2 * S::PB; o += 16 * S::kThreads) {
