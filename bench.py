@@ -528,6 +528,20 @@ def leg(torch, stream, launch, warmup: int, steps: int) -> dict:
     return r
 
 
+def paired_legs(torch, stream, launch_a, launch_b, rounds: int = 8, group: int = 50) -> dict:
+    """Two entry points in alternating groups of `group` launches (a, b, a,
+    b, ...), so that both see the same clock: the mean launch time of each
+    (ms) and their difference (us), with the per-round differences."""
+    ta, tb = [], []
+    for _ in range(rounds):
+        ta.append(timed_launches(torch, stream, launch_a, group, group)["mean_ms"])
+        tb.append(timed_launches(torch, stream, launch_b, group, group)["mean_ms"])
+    diff = [1e3 * (b - a) for a, b in zip(ta, tb)]
+    return {"a_mean_ms": float(np.mean(ta)), "b_mean_ms": float(np.mean(tb)),
+            "b_minus_a_us": float(np.mean(diff)), "b_minus_a_us_per_round": [round(x, 3) for x in diff],
+            "rounds": rounds, "group": group}
+
+
 def mse_summary(torch, R, x, c, sigma, outlier_tokens, n: int) -> dict:
     """Quantization MSE of the GPU's own outputs on the first 1024 tokens, in
     the rotated domain: mean over channels of (y - dequant(codes))^2 with y
@@ -673,6 +687,10 @@ def main() -> int:
     ceiling = leg(torch, stream, cstep, 100, aux_steps)
     dvec = leg(torch, stream, dstep, 100, aux_steps)
     zint = leg(torch, stream, zstep, 100, aux_steps)
+    # the d-vector entry point against the headline's (c, sigma) one under the
+    # same clock (before the headline's warm-up, so that the last launches of
+    # the process are the timed ones)
+    dpair = paired_legs(torch, stream, step, dstep)
 
     for i in range(args.warmup):
         step(i)
@@ -725,6 +743,11 @@ def main() -> int:
             "entry_point": "signrot_rotate_quant_int4_outlier (d = sigma * row c of H, from calibration)",
             "d_vector_entry_point_kernel_avg_ms": dvec["mean_ms"],
             "d_vector_entry_point_launch_ms": dvec,
+            "d_vector_minus_c_sigma_paired": {
+                "c_sigma_mean_ms": dpair["a_mean_ms"], "d_vector_mean_ms": dpair["b_mean_ms"],
+                "difference_us": dpair["b_minus_a_us"], "per_round_us": dpair["b_minus_a_us_per_round"],
+                "launches": f"{dpair['rounds']} rounds of {dpair['group']} + {dpair['group']}, alternating, before "
+                            "the headline's warm-up"},
             "integer_zero_point_variant_kernel_avg_ms": zint["mean_ms"],
             "integer_zero_point_variant_launch_ms": zint,
             "launch_ms": {k: head[k] for k in ("mean_ms", "p10_ms", "p50_ms", "p90_ms", "group")},
