@@ -135,8 +135,12 @@ __device__ inline void build_dbits(const int8_t* d, int n, uint32_t* dbits) {
 
 // Same decision as decode_d_form, in parallel, for k >= 5 (a 32-bit word of
 // the mask then lies inside one block of 2^k channels).  h28 holds the row
-// masks of H28 in LDS.  Every thread of the block must call it.  THREADS: the
-// block size when the caller knows it at compile time (else 0: blockDim.x).
+// masks of H28 in LDS.  Every thread of the block must call it, after a
+// barrier that published the whole bitmask; before that barrier the caller
+// sets sh_scratch[3] = 0 (the flag a thread raises when an entry is off the
+// form).  Each wave decides the candidate form itself from the bitmask, so
+// only one more barrier follows.  THREADS: the block size when the caller
+// knows it at compile time (else 0: blockDim.x).
 template <int THREADS = 0>
 __device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbits, const uint32_t* h28,
                                            int* sh_scratch) {
@@ -144,42 +148,35 @@ __device__ inline DForm decode_d_form_fast(const RqArgs& a, const uint32_t* dbit
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   auto dbit = [&](int j) -> uint32_t { return (dbits[j >> 5] >> (j & 31)) & 1u; };
-  if (tid < 64) {
-    const uint32_t d0 = dbit(0);
-    // bit t of c_b: sign change between b = 0 and b = 2^t (first block)
-    const unsigned long long cbm = __ballot(lane < a.k && dbit(1 << lane) != d0);
-    const int cb = static_cast<int>(cbm & ((1ull << a.k) - 1ull));
-    int ca = 0, found = 1;
-    if (a.m28) {
-      // normalised first column of each block against each normalised H28 row
-      const unsigned long long em = __ballot(lane < 28 && (dbit(lane << a.k) ^ d0) != 0u);
-      const uint32_t e = static_cast<uint32_t>(em);
-      uint32_t norm = 0xffffffffu;
-      if (lane < 28) {
-        const uint32_t m = h28[lane];
-        norm = (m & 1u) ? (~m & 0x0fffffffu) : m;
-      }
-      const unsigned long long hit = __ballot(lane < 28 && norm == e);
-      found = hit != 0ull;
-      ca = found ? __builtin_ctzll(hit) : 0;
+  const uint32_t d0 = dbit(0);
+  // bit t of c_b: sign change between b = 0 and b = 2^t (first block)
+  const unsigned long long cbm = __ballot(lane < a.k && dbit(1 << lane) != d0);
+  const int cb = static_cast<int>(cbm & ((1ull << a.k) - 1ull));
+  int ca = 0, found = 1;
+  if (a.m28) {
+    // normalised first column of each block against each normalised H28 row
+    const unsigned long long em = __ballot(lane < 28 && (dbit(lane << a.k) ^ d0) != 0u);
+    const uint32_t e = static_cast<uint32_t>(em);
+    uint32_t norm = 0xffffffffu;
+    if (lane < 28) {
+      const uint32_t m = h28[lane];
+      norm = (m & 1u) ? (~m & 0x0fffffffu) : m;
     }
-    if (tid == 0) {
-      sh_scratch[0] = found;
-      sh_scratch[1] = (ca << a.k) | cb;
-      sh_scratch[2] = static_cast<int>(d0 ^ (a.m28 ? (h28[ca] & 1u) : 0u));
-      sh_scratch[3] = 0;  // set by any thread that finds an entry off the form
-    }
+    const unsigned long long hit = __ballot(lane < 28 && norm == e);
+    found = hit != 0ull;
+    ca = found ? __builtin_ctzll(hit) : 0;
   }
-  __syncthreads();
-  DForm f{sh_scratch[0], sh_scratch[1], sh_scratch[2]};
+  DForm f{found, (ca << a.k) | cb, static_cast<int>(d0 ^ (a.m28 ? (h28[ca] & 1u) : 0u))};
   if (f.structured) {
     const int bmask = (1 << a.k) - 1;
-    const int cb = f.c & bmask;
-    const int ca = f.c >> a.k;
-    // parity(cb & i) for i = 0..31, as a word
+    // parity(cb & i) for i = 0..31, as a word: the XOR of the index-bit
+    // patterns of the set bits of cb & 31
     uint32_t pw = 0u;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) pw |= (__popc(static_cast<uint32_t>(cb & i)) & 1u) << i;
+    if (cb & 1) pw ^= 0xAAAAAAAAu;
+    if (cb & 2) pw ^= 0xCCCCCCCCu;
+    if (cb & 4) pw ^= 0xF0F0F0F0u;
+    if (cb & 8) pw ^= 0xFF00FF00u;
+    if (cb & 16) pw ^= 0xFFFF0000u;
     for (int w = tid; w < a.n / 32; w += nthreads) {
       const int j0 = 32 * w;
       uint32_t flip = static_cast<uint32_t>(f.neg) ^ (__popc(static_cast<uint32_t>(cb & j0 & bmask)) & 1u);

@@ -522,6 +522,7 @@ void rq_fast_kernel(RqArgs a) {
         [&] {
           // the bitmask of d in LDS, bit j set when d_j = -1
           if (tid < kWords) dbits[tid] = sign_word_of(dlo, dhi);
+          if (tid == 0) scratch[3] = 0;  // the form check's flag
           for (int wd = tid + S::kThreads; wd < kWords; wd += S::kThreads) dbits[wd] = sign_word(a.d + 32 * wd);
           __syncthreads();
           return decode_d_form_fast<S::kThreads>(a, dbits, h28_lds, scratch);

@@ -403,6 +403,7 @@ void rq_halves_kernel(RqArgs a) {
     form = DForm{1, a.form_c, a.form_neg};
   } else {
     build_dbits(a.d, a.n, dbits);
+    if (tid == 0) scratch[3] = 0;  // the form check's flag
     __syncthreads();
     form = decode_d_form_fast(a, dbits, h28_lds, scratch);
   }
